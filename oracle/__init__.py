@@ -1,0 +1,15 @@
+"""FP64 CPU oracle for paged GQA decode attention (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The HIP library neither imports nor falls
+back to it.
+"""
+
+from .decode import (  # noqa: F401
+    attend,
+    contiguous_decode_attention,
+    gather_sequence,
+    lse_merge,
+    paged_decode_attention,
+    partial_attention,
+)
