@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of paged GQA decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 400] [--warmup 40]
+
+Workload (the bandwidth-stress configuration): batch 16, every context 4096
+tokens, 40 query heads over 8 KV heads, head_dim 128, 128-token pages, BF16
+K/V. Forty layers each own a 512-page K and V pool (268 MB of K+V per layer,
+10.7 GB in all) and q/out; the block table and context lengths are shared by
+all layers. A step is one pa_decode call (partition + reduce kernels) on one
+layer; steps cycle through the 40 layers, so every call reads its K/V from HBM
+(the 39 other layers evict it from the 256 MB Infinity Cache). Layer 0 is
+drawn on the CPU and checked against the FP64 oracle after the timed region;
+layers 1-39 are drawn on the GPU (timing only).
+
+Printed: one JSON line with KV-read throughput (GB/s of K+V bytes the calls
+must read, whole job), the per-call time, the roofline of the partition
+kernel (timed alone with HIP events over the same rotation), the oracle timed
+on the host cores on a bounded sample, and per-call times of the other
+standard workloads.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "paged GQA decode attention: µs/call and KV-read GB/s (% of HBM peak)"
+KERNEL_SRC = os.path.join(ROOT, "paged_gqa_attention_amd", "csrc", "decode_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_kernel_config3_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400, help="timed pa_decode calls")
+    ap.add_argument("--warmup", type=int, default=40, help="untimed calls first")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+class Decoder:
+    """Pre-marshalled C-ABI calls (the binding's checks run once, not per call)."""
+
+    def __init__(self, pa, q, k, v, bt, ctx, out, ws, scale, shape, stream):
+        import ctypes
+        self.pa = pa
+        self.args = (ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     bt.data_ptr(), ctx.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
+                     ws.data_ptr(), ws.numel(), stream)
+        self.pargs = (ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                      bt.data_ptr(), ctx.data_ptr(), ctypes.c_float(scale), ws.data_ptr(),
+                      ws.numel(), stream)
+
+    def decode(self):
+        st = self.pa.lib.pa_decode(*self.args)
+        if st:
+            raise self.pa.PagedAttnError(st, "pa_decode")
+
+    def partials(self):
+        st = self.pa.lib.pa_decode_partials(*self.pargs)
+        if st:
+            raise self.pa.PagedAttnError(st, "pa_decode_partials")
+
+
+def timed(torch, fns, steps, warmup):
+    """Average ms per call over `steps` calls cycling through `fns`."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fns[i % len(fns)]()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence, KV head or page range; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_gqa_attention_amd import pagedattn as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+
+    # ---- the 40-layer bandwidth-stress workload ---------------------------
+    L = workloads.CONFIG3_LAYERS
+    w0 = workloads.config(3)
+    B, Hq, D = w0.q.shape
+    N, P, Hkv, _ = w0.k_cache.shape
+    bt = w0.block_table.to(dev)
+    ctx = w0.context_lens.to(dev)
+    gen = torch.Generator(device=dev).manual_seed(3003)
+    layers = []
+    for li in range(L):
+        if li == 0:
+            q, k, v = w0.q.to(dev), w0.k_cache.to(dev), w0.v_cache.to(dev)
+        else:
+            q = torch.randn(w0.q.shape, device=dev, generator=gen).to(torch.bfloat16)
+            k = torch.randn(w0.k_cache.shape, device=dev, generator=gen).to(torch.bfloat16)
+            v = torch.randn(w0.v_cache.shape, device=dev, generator=gen).to(torch.bfloat16)
+        layers.append((q, k, v, torch.empty_like(q)))
+    torch.cuda.synchronize()
+    print(f"[bench] {L} layers resident ({L * 2 * w0.k_cache.numel() * 2 / 1e9:.1f} GB K+V)",
+          file=sys.stderr, flush=True)
+
+    shape = pa.shape_of(w0.q, w0.k_cache, w0.block_table)
+    plan = pa.pa_plan(shape)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    decs = [Decoder(pa, q, k, v, bt, ctx, o, ws, w0.scale, shape, stream) for (q, k, v, o) in layers]
+    kv_bytes = w0.kv_bytes()  # 4096 B per (sequence, token) x 65536 tokens
+
+    ms_call = timed(torch, [d.decode for d in decs], args.steps, args.warmup)
+    ms_part = timed(torch, [d.partials for d in decs], args.steps, args.warmup)
+    # leave layer 0's output from a full call for the parity check
+    decs[0].decode()
+    torch.cuda.synchronize()
+    out0 = layers[0][3].cpu()
+    print(f"[bench] {ms_call * 1e3:.2f} us/call, partition kernel {ms_part * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+
+    gbs = kv_bytes / (ms_call * 1e-3) / 1e9
+    part_gbs = kv_bytes / (ms_part * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha256_16") == kernel_source_hash():
+            traffic = t.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 5),
+        "us_per_call": round(ms_call * 1e3, 2),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "bandwidth stress: batch 16 x context 4096, Hq 40 / Hkv 8, head_dim 128, "
+                        "128-token pages, 40 layers' 512-page pools called back to back",
+            "batch": B, "context": int(w0.context_lens.max()), "num_q_heads": Hq,
+            "num_kv_heads": Hkv, "head_dim": D, "page_size": P, "layers": L,
+            "split_pages": plan.split_pages, "num_splits": plan.num_splits,
+            "kv_bytes_per_call": kv_bytes,
+        },
+        "roofline": {
+            "kernel": "partition_kernel<128,5>",
+            "bound": "hbm",
+            "achieved": round(part_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "us_per_launch": round(ms_part * 1e3, 2),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+
+    # ---- layer-0 parity and the oracle on the host cores -------------------
+    import oracle
+
+    t_start = time.perf_counter()
+    ref = oracle.paged_decode_attention(w0.q, w0.k_cache, w0.v_cache, w0.block_table,
+                                        w0.context_lens, w0.scale)
+    t_one = time.perf_counter() - t_start
+    g = out0.float().numpy().astype(np.float64)
+    err = np.abs(g - ref)
+    result["parity_layer0"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                               "gate_max_abs": 2e-2, "gate_mean_abs": 2e-3,
+                               "finite": bool(np.isfinite(g).all())}
+    if not args.no_cpu_baseline:
+        runs, total = 1, t_one
+        while total < args.cpu_seconds:
+            t1 = time.perf_counter()
+            oracle.paged_decode_attention(w0.q, w0.k_cache, w0.v_cache, w0.block_table,
+                                          w0.context_lens, w0.scale)
+            total += time.perf_counter() - t1
+            runs += 1
+        cpu_gbs = kv_bytes * runs / total / 1e9
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"FP64 numpy oracle on layer 0 of the same workload (16 x 4096 tokens, "
+                      f"{kv_bytes} K+V bytes per call), {runs} calls in {total:.1f} s; "
+                      f"includes the BF16->FP64 page gather",
+            "seconds_per_call": round(total / runs, 3),
+            "host": {"cpu": cpu_model(), "os_cpu_count": os.cpu_count(),
+                     "affinity_cores": len(os.sched_getaffinity(0))},
+            "gpu_speedup": round(cpu_gbs and gbs / cpu_gbs, 1),
+        }
+
+    # ---- the other standard workloads (per-call time, cold rotation) --------
+    del layers, decs
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra = {}
+        for cfg, copies in ((1, 1), (2, 8), (4, 2), (5, 8)):
+            w = workloads.config(cfg)
+            shp = pa.shape_of(w.q, w.k_cache, w.block_table)
+            pl = pa.pa_plan(shp)
+            wsx = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device=dev)
+            btx, ctxx = w.block_table.to(dev), w.context_lens.to(dev)
+            sets = []
+            for _ in range(copies):
+                qx = w.q.to(dev)
+                sets.append((qx, w.k_cache.to(dev), w.v_cache.to(dev), torch.empty_like(qx)))
+            ds = [Decoder(pa, *s[:3], btx, ctxx, s[3], wsx, w.scale, shp, stream) for s in sets]
+            steps = 200 if cfg != 4 else 60
+            ms = timed(torch, [d.decode for d in ds], steps, max(4, copies))
+            by = w.kv_bytes()
+            extra[f"config{cfg}"] = {
+                "description": workloads.CONFIG_DESCRIPTIONS[cfg],
+                "us_per_call": round(ms * 1e3, 2),
+                "kv_bytes_per_call": by,
+                "kv_gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "rotation_copies": copies,
+                "split_pages": pl.split_pages,
+            }
+            print(f"[bench] config{cfg}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+            del sets, ds, wsx
+            torch.cuda.empty_cache()
+        result["other_workloads"] = extra
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 1 << 30
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

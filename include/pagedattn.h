@@ -1,0 +1,166 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn: single-token (decode) GQA attention over
+ * a paged BF16 K/V cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ *   For every sequence b and query head hq, with G = num_q_heads / num_kv_heads
+ *   and KV head h = hq / G (consecutive grouping):
+ *
+ *     out[b, hq, :] = softmax_t( scale * q[b, hq, :] . K_b[t, h, :] ) @ V_b[t, h, :]
+ *
+ *   over the tokens t in [0, context_lens[b]) of sequence b. This is the full
+ *   (no window, no sinks) GQA attention of "Qwen 3" (TensorSharp docs),
+ *   section 3 "Forward graph" and section 4.1 "Attention", where Q is scaled
+ *   by 1/sqrt(head_dim) and attends to everything cached so far, the new
+ *   token included.
+ *
+ * Data layouts (all row-major, contiguous, caller-owned device memory)
+ *   q, out        BF16 [batch, num_q_heads, head_dim]: one active token per
+ *                 sequence, the "active TND" Q/O of "Qwen3-14B" (pypto-lib
+ *                 models page), "decode_fwd" section.
+ *   k_cache,      BF16 [num_pages, page_size, num_kv_heads, head_dim]: flat
+ *   v_cache       paged pools in [page, token, kv_head, dim] byte order (same
+ *                 page and section). Separate K and V pools; they may alias.
+ *   block_table   INT32 [batch, max_pages_per_seq]: token t of sequence b is in
+ *                 page block_table[b][t / page_size] at slot t % page_size
+ *                 ("Qwen 3" TensorSharp docs, section 11: block id times block
+ *                 size plus offset, gathered from block tables and lengths).
+ *                 Only the first ceil(context_lens[b] / page_size) entries of a
+ *                 row are read; the rest may hold -1 or anything.
+ *   context_lens  INT32 [batch]: tokens cached for each sequence, in
+ *                 [0, max_pages_per_seq * page_size]. 0 gives an output row of
+ *                 exact zeros (the empty-row convention of the orcarouter page on
+ *                 the Ascend QSA adapter).
+ *
+ * Supported shapes
+ *   page_size == 128 (the 128-token pages of the "Qwen3-14B" deployment
+ *   table), head_dim in {128, 256}, 1 <= num_q_heads / num_kv_heads <= 16
+ *   (covers 40/8 of Qwen3-14B and every local head pair the orcarouter page
+ *   lists for head_dim 256: (16,2), (24,2), (12,1), (6,1), (3,1)).
+ *   Anything else returns PA_ERR_UNSUPPORTED.
+ *
+ * Ownership, synchronisation, errors
+ *   - Every pointer argument except `shape`/`plan`/`bytes` is a device pointer
+ *     owned by the caller. The library allocates nothing, keeps no pointer after
+ *     returning and needs the buffers alive until the stream has run the work.
+ *   - pa_decode only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     default stream). It never copies device data to the host and never
+ *     synchronises, so it can be captured into a HIP graph.
+ *   - Arguments are validated on the host; a bad argument returns a status code
+ *     before anything is launched. Nothing is printed, nothing aborts, there is
+ *     no fallback path.
+ *   - Device data is not validated on the host (that would need a copy back).
+ *     In the kernels: a block-table entry outside [0, num_pages) among the
+ *     entries a sequence needs, or a context length outside
+ *     [0, max_pages_per_seq * page_size], never causes an out-of-bounds read;
+ *     the affected output rows are set to NaN instead.
+ *   - Several sequences may share physical pages. `out` must not overlap q, the
+ *     caches or the workspace. Concurrent calls need separate workspaces.
+ *   - Results are bit-identical from run to run for the same inputs and plan
+ *     (no atomics, fixed reduction order).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_PAGE_SIZE 128
+#define PA_MAX_GQA_RATIO 16
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  PA_ERR_INVALID_ARGUMENT = 2,    /* negative/inconsistent sizes, misaligned pointer, non-finite scale */
+  PA_ERR_UNSUPPORTED = 3,         /* valid but unsupported page size, head_dim or GQA ratio */
+  PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < pa_workspace_size() */
+  PA_ERR_LAUNCH = 5               /* the HIP runtime rejected a kernel launch */
+} pa_status_t;
+
+/* Problem description. All fields are host integers. */
+typedef struct {
+  int32_t batch;              /* B >= 0 (B == 0: nothing to do, PA_OK)          */
+  int32_t num_q_heads;        /* Hq >= 1, multiple of num_kv_heads              */
+  int32_t num_kv_heads;       /* Hkv >= 1                                       */
+  int32_t head_dim;           /* D in {128, 256}                                */
+  int32_t page_size;          /* P == 128                                       */
+  int32_t max_pages_per_seq;  /* W >= 1: row length (stride) of block_table     */
+  int32_t num_pages;          /* N >= 1: pages in each of k_cache and v_cache   */
+  int32_t split_pages;        /* pages per split; 0 lets the library choose     */
+} pa_shape_t;
+
+/* The launch plan the library derives from a shape (host arithmetic only). */
+typedef struct {
+  int32_t split_pages;        /* pages of context each split covers             */
+  int32_t num_splits;         /* ceil(max_pages_per_seq / split_pages)          */
+  size_t workspace_bytes;     /* bytes pa_decode needs in `workspace`           */
+} pa_plan_t;
+
+/* Version of this ABI (PA_ABI_VERSION of the built library). */
+int pa_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* pa_status_string(int status);
+
+/* Fill `plan` for `shape`. The plan depends only on the shape (never on device
+ * data such as context_lens), so it can be computed once and reused. */
+pa_status_t pa_plan(const pa_shape_t* shape, pa_plan_t* plan);
+
+/* Bytes of device workspace pa_decode needs for `shape` (FP32 split partials:
+ * unnormalised output rows and the running max / sum per split). */
+pa_status_t pa_workspace_size(const pa_shape_t* shape, size_t* bytes);
+
+/* Enqueue decode attention on `stream`.
+ *   q            device, BF16 [B, Hq, D], 16-byte aligned
+ *   k_cache      device, BF16 [N, P, Hkv, D], 16-byte aligned
+ *   v_cache      device, BF16 [N, P, Hkv, D], 16-byte aligned (may equal k_cache)
+ *   block_table  device, INT32 [B, W]
+ *   context_lens device, INT32 [B]
+ *   scale        finite FP32 logit scale, normally 1/sqrt(D)
+ *   out          device, BF16 [B, Hq, D], 16-byte aligned; written with FP32
+ *                results rounded to nearest even
+ *   workspace    device, >= pa_workspace_size() bytes, 256-byte aligned
+ *   stream       hipStream_t (NULL = default stream)
+ * Returns PA_OK once both kernels are enqueued. */
+pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table,
+                      const int32_t* context_lens, float scale, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of pa_decode, for callers that move or combine split partials
+ * themselves (for instance a context-parallel decode that gives each GPU a
+ * range of pages and merges the partials after exchanging them).
+ *
+ * Workspace layout (FP32), with S = plan.num_splits and T = page_size *
+ * plan.split_pages: split s covers tokens [s*T, (s+1)*T) of a sequence, and
+ * with s_t = scale * log2(e) * (q . k_t) over the split's tokens t < ctx,
+ *   acc [B][Hq][S][D] at byte 0:        sum_t 2^(s_t - m) * v_t
+ *   ml  [B][Hq][S][2] at byte align256(B*Hq*S*D*4):  { m = max_t s_t,
+ *                                                      l = sum_t 2^(s_t - m) }
+ * Only splits with s*T < context_lens[b] are written (partials) and read
+ * (merge). The merge is the log-sum-exp combination of these partials:
+ * out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s,
+ * rounded to BF16; context 0 gives zeros. */
+
+/* Stage 1: write the split partials of every (sequence, query head) to the
+ * workspace. Same arguments and checks as pa_decode, without `out`. */
+pa_status_t pa_decode_partials(const pa_shape_t* shape, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Stage 2: merge the partials in `workspace` into out (BF16 [B, Hq, D]). */
+pa_status_t pa_merge_partials(const pa_shape_t* shape, const int32_t* context_lens,
+                              const void* workspace, size_t workspace_bytes, void* out,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

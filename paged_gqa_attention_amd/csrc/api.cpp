@@ -1,0 +1,219 @@
+// C-ABI entry points of libpagedattn: argument validation, the split plan and
+// the call into the kernel launchers. Host code only; it never reads device
+// memory and never synchronises.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "pagedattn.h"
+
+namespace {
+
+// MI355X has 256 compute units. The plan aims for at least four 4-wave
+// workgroups per CU when the sequence lengths are at their maximum.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kTargetWorkgroups = 4 * kComputeUnits;
+// The automatic plan keeps a split's score tile within 16 KiB of LDS so that
+// several workgroups fit on a CU; an explicit split_pages may use up to 64 KiB.
+constexpr size_t kAutoLdsScoreBytes = 16 * 1024;
+constexpr size_t kMaxLdsBytes = 64 * 1024;
+
+int head_pad(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+pa_status_t check_shape(const pa_shape_t* s) {
+  if (!s) return PA_ERR_NULL_POINTER;
+  if (s->batch < 0 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 ||
+      s->page_size < 1 || s->max_pages_per_seq < 1 || s->num_pages < 1 || s->split_pages < 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (s->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+  const int g = s->num_q_heads / s->num_kv_heads;
+  if (!pa::has_kernels(s->head_dim, g)) return PA_ERR_UNSUPPORTED;
+  // grid limits (batch and KV heads are grid dimensions) and 32-bit offsets
+  // inside one page / one block-table row
+  if (s->batch > 65535 || s->num_kv_heads > 4096 || s->max_pages_per_seq > (1 << 20))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Pages per split. Never looks at context lengths (they live on the device).
+int choose_split_pages(const pa_shape_t* s) {
+  const int g = s->num_q_heads / s->num_kv_heads;
+  const int w = s->max_pages_per_seq;
+  const size_t row_bytes = sizeof(float) * (size_t)head_pad(g) * PA_PAGE_SIZE;  // per page
+  int pps;
+  if (s->split_pages > 0) {
+    pps = s->split_pages;
+    int cap = 1;
+    while (cap < w && pa::partition_lds_bytes(s->head_dim, g, cap + 1) <= kMaxLdsBytes) ++cap;
+    if (pps > cap) pps = cap;
+  } else {
+    const int64_t pairs = (int64_t)(s->batch > 0 ? s->batch : 1) * s->num_kv_heads;
+    const int64_t splits_wanted = (kTargetWorkgroups + pairs - 1) / pairs;
+    pps = (int)((w + splits_wanted - 1) / splits_wanted);
+    const int cap = (int)(kAutoLdsScoreBytes / row_bytes);
+    if (pps > cap) pps = cap > 0 ? cap : 1;
+  }
+  if (pps > w) pps = w;
+  if (pps < 1) pps = 1;
+  return pps;
+}
+
+pa_status_t make_plan(const pa_shape_t* s, pa_plan_t* p) {
+  const int pps = choose_split_pages(s);
+  const int splits = (s->max_pages_per_seq + pps - 1) / pps;
+  const size_t rows = (size_t)s->batch * s->num_q_heads * splits;
+  p->split_pages = pps;
+  p->num_splits = splits;
+  p->workspace_bytes = align_up(rows * s->head_dim * sizeof(float), 256) +
+                       align_up(rows * 2 * sizeof(float), 256);
+  return PA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK:
+      return "PA_OK: success";
+    case PA_ERR_NULL_POINTER:
+      return "PA_ERR_NULL_POINTER: a required pointer is NULL";
+    case PA_ERR_INVALID_ARGUMENT:
+      return "PA_ERR_INVALID_ARGUMENT: invalid size, alignment or scale";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: page size, head_dim or GQA ratio not supported";
+    case PA_ERR_WORKSPACE_TOO_SMALL:
+      return "PA_ERR_WORKSPACE_TOO_SMALL: workspace smaller than pa_workspace_size()";
+    case PA_ERR_LAUNCH:
+      return "PA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    default:
+      return "unknown pa_status_t value";
+  }
+}
+
+pa_status_t pa_plan(const pa_shape_t* shape, pa_plan_t* plan) {
+  if (!plan) return PA_ERR_NULL_POINTER;
+  const pa_status_t st = check_shape(shape);
+  if (st != PA_OK) return st;
+  return make_plan(shape, plan);
+}
+
+pa_status_t pa_workspace_size(const pa_shape_t* shape, size_t* bytes) {
+  if (!bytes) return PA_ERR_NULL_POINTER;
+  pa_plan_t plan;
+  const pa_status_t st = pa_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  *bytes = plan.workspace_bytes;
+  return PA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the workspace and of the arguments every stage takes;
+// fills the launch arguments. `need_inputs` / `need_out` select which device
+// pointers the stage reads or writes.
+pa_status_t prepare(const pa_shape_t* shape, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* context_lens, float scale, void* out, const void* workspace,
+                    size_t workspace_bytes, void* stream, bool need_inputs, bool need_out,
+                    pa::LaunchArgs* a) {
+  if (need_inputs) {
+    if (!q || !k_cache || !v_cache || !block_table) return PA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)block_table & 3u))
+      return PA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  }
+  if (!context_lens) return PA_ERR_NULL_POINTER;
+  if ((uintptr_t)context_lens & 3u) return PA_ERR_INVALID_ARGUMENT;
+  if (need_out) {
+    if (!out) return PA_ERR_NULL_POINTER;
+    if (!aligned16(out)) return PA_ERR_INVALID_ARGUMENT;
+  }
+  pa_plan_t plan;
+  make_plan(shape, &plan);
+  if (!workspace) return PA_ERR_NULL_POINTER;
+  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < plan.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+
+  const size_t rows = (size_t)shape->batch * shape->num_q_heads * plan.num_splits;
+  a->q = static_cast<const uint16_t*>(q);
+  a->k_cache = static_cast<const uint16_t*>(k_cache);
+  a->v_cache = static_cast<const uint16_t*>(v_cache);
+  a->block_table = block_table;
+  a->context_lens = context_lens;
+  a->out = static_cast<uint16_t*>(out);
+  a->ws_acc = static_cast<float*>(const_cast<void*>(workspace));
+  a->ws_ml = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                      align_up(rows * shape->head_dim * sizeof(float), 256));
+  a->batch = shape->batch;
+  a->num_q_heads = shape->num_q_heads;
+  a->num_kv_heads = shape->num_kv_heads;
+  a->head_dim = shape->head_dim;
+  a->max_pages = shape->max_pages_per_seq;
+  a->num_pages = shape->num_pages;
+  a->split_pages = plan.split_pages;
+  a->num_splits = plan.num_splits;
+  a->score_scale = scale * 1.4426950408889634f;  // natural-exp softmax computed as exp2
+  a->stream = stream;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table,
+                      const int32_t* context_lens, float scale, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0) return PA_OK;
+  pa::LaunchArgs a;
+  st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, out, workspace,
+               workspace_bytes, stream, true, true, &a);
+  if (st != PA_OK) return st;
+  if (pa::launch_partition(a) != 0) return PA_ERR_LAUNCH;
+  return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status_t pa_decode_partials(const pa_shape_t* shape, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0) return PA_OK;
+  pa::LaunchArgs a;
+  st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, nullptr, workspace,
+               workspace_bytes, stream, true, false, &a);
+  if (st != PA_OK) return st;
+  return pa::launch_partition(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status_t pa_merge_partials(const pa_shape_t* shape, const int32_t* context_lens,
+                              const void* workspace, size_t workspace_bytes, void* out,
+                              void* stream) {
+  pa_status_t st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0) return PA_OK;
+  pa::LaunchArgs a;
+  st = prepare(shape, nullptr, nullptr, nullptr, nullptr, context_lens, 1.0f, out, workspace,
+               workspace_bytes, stream, false, true, &a);
+  if (st != PA_OK) return st;
+  return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,470 @@
+// Paged GQA decode attention for gfx950 (MI355X): split-K partition kernel and
+// log-sum-exp reduce kernel.
+//
+// The operation (full softmax attention of one query token per sequence over
+// its cached K/V, with query head hq reading KV head hq / G) is the one of
+// "Qwen 3" (TensorSharp docs), sections 3 "Forward graph" and 4.1 "Attention".
+// The cache is the flat paged pool of "Qwen3-14B" (pypto-lib models page),
+// "decode_fwd" section: [page, token, kv_head, dim], reached through a block
+// table ("Qwen 3" TensorSharp docs, section 11).
+//
+// Work decomposition
+//   partition_kernel<D, G>: one workgroup (4 waves) per (split s, KV head h,
+//   sequence b). A split is `split_pages` consecutive pages of the sequence.
+//   1. q . K^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with the G query
+//      heads of the group as the 16 rows of A (zero padded) and 16 tokens as
+//      the columns of B. Each lane loads 64 contiguous bytes of one token row
+//      per MFMA k-step, so one load instruction covers 16 rows x 64 B.
+//      Scores are scaled by scale*log2(e) in FP32, tail slots are masked by
+//      select, and the [token][head] score tile goes to LDS.
+//   2. Per head: max over the split, p = 2^(s - max), l = sum p (FP32, fixed
+//      order), all in LDS.
+//   3. P.V on the vector ALUs in FP32: each load instruction reads whole token
+//      rows (16 lanes x 16 B for D=128), every lane accumulates G heads x 8
+//      dims, then rows and waves are summed in a fixed order.
+//   The unnormalised output, the max and the sum of each split go to an FP32
+//   workspace.
+//   reduce_kernel<D>: one workgroup per (query head, sequence) merges the
+//   splits that cover the context: M = max m_s, out = sum 2^(m_s-M) acc_s /
+//   sum 2^(m_s-M) l_s, rounded to BF16 (nearest even).
+//
+// Nothing here uses atomics; the reduction order is fixed, so repeated calls
+// give bit-identical results.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace pa {
+namespace {
+
+constexpr int kPage = 128;      // tokens per page
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kWaves = kThreads / 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// BF16 -> FP32 is exact: the BF16 bits are the high half of the FP32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 -> BF16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Score row stride in LDS: G padded to a power of two >= 4, so that one
+// 16-byte store per MFMA lane group lands a whole group of 4 heads.
+template <int G>
+struct HeadPad {
+  static constexpr int value = G <= 4 ? 4 : (G <= 8 ? 8 : 16);
+};
+
+// LDS of the partition kernel, in 4-byte words:
+//   [score tile: split_tokens x GP floats, reused as 2 x G x D partial sums]
+//   [cross-wave scratch: 2 x 4 waves x 16 floats]
+//   [page ids of the split: split_pages ints]
+template <int D, int G>
+__host__ __device__ constexpr int lds_tile_words(int split_pages) {
+  return split_pages * kPage * HeadPad<G>::value > 2 * G * D
+             ? split_pages * kPage * HeadPad<G>::value
+             : 2 * G * D;
+}
+constexpr int kRedWords = 2 * kWaves * 16;
+
+template <int D, int G>
+__host__ __device__ constexpr int lds_words(int split_pages) {
+  return lds_tile_words<D, G>(split_pages) + kRedWords + split_pages;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void partition_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, int num_kv_heads, int max_pages, int num_pages,
+    int split_pages, int num_splits, float score_scale) {
+  static_assert(D == 128 || D == 256, "head_dim");
+  static_assert(G >= 1 && G <= 16, "gqa ratio");
+  constexpr int GP = HeadPad<G>::value;   // LDS row stride (floats)
+  constexpr int GQ = (G + 3) / 4;         // MFMA lane groups holding real heads
+  constexpr int KK = D / 32;              // MFMA k-steps per 16-token tile
+  constexpr int LPR = D / 8;              // lanes per token row in P.V
+  constexpr int RPI = 64 / LPR;           // token rows per load instruction in P.V
+  constexpr int PV_U = 4;                 // load instructions per P.V block
+  constexpr int BR = RPI * PV_U;          // token rows per P.V block (16 or 8)
+  static_assert(16 % BR == 0, "P.V blocks must tile the 16-token score tiles");
+
+  extern __shared__ float smem[];
+
+  const int s = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int num_q_heads = num_kv_heads * G;
+  const int split_tokens = split_pages * kPage;
+  int ctx = context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
+  const int t0 = s * split_tokens;  // first token of this split
+  const int n_s = min(ctx - t0, split_tokens);
+  if (n_s <= 0) return;  // split past the context: nothing to write
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lq = lane >> 4;  // MFMA lane group (0..3)
+  const int lr = lane & 15;  // MFMA row / column inside the group
+
+  float* s_tile = smem;                                        // [tiles*16][GP]
+  float* red = smem + lds_tile_words<D, G>(split_pages);       // [2][4][16]
+  int* s_page = reinterpret_cast<int*>(red + kRedWords);       // [split_pages]
+
+  // Page ids this split needs, read once; an id outside the pool becomes -1.
+  const int npg = (n_s + kPage - 1) / kPage;
+  if ((int)threadIdx.x < npg) {
+    const int page = block_table[(size_t)b * max_pages + (size_t)s * split_pages + threadIdx.x];
+    s_page[threadIdx.x] = (unsigned)page < (unsigned)num_pages ? page : -1;
+  }
+
+  // A operand of the score MFMA: lane (lq, lr) holds q[head lr][32*kk + 8*lq .. +7]
+  // (zero rows for heads >= G).
+  u32x4 qa[KK];
+  {
+    const uint16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)h * G + lr) * D + 8 * lq;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qa[kk] = (lr < G) ? load16(qrow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+
+  const size_t page_bytes = (size_t)kPage * num_kv_heads * D * sizeof(uint16_t);
+  const uint32_t row_bytes = (uint32_t)num_kv_heads * D * sizeof(uint16_t);  // token stride
+  const uint32_t head_bytes = (uint32_t)h * D * sizeof(uint16_t);
+
+  // Base of the page holding local token tl (wave-uniform); bad -> pool start.
+  auto page_base = [&](const uint16_t* pool, int tl, bool& bad) -> const char* {
+    const int page = __builtin_amdgcn_readfirstlane(s_page[tl >> 7]);
+    bad = page < 0;
+    return reinterpret_cast<const char*>(pool) + (size_t)(bad ? 0 : page) * page_bytes;
+  };
+
+  // ---- phase 1: scores = q . K^T on MFMA --------------------------------
+  // B operand: lane (lq, lr) holds K[token tl + lr][32*kk + 8*lq .. +7]; one
+  // load instruction covers 16 token rows x 64 contiguous bytes.
+  const uint32_t k_lane_off = (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
+  auto load_k = [&](int tile, u32x4 (&buf)[KK], bool& bad) {
+    const int tl = tile * 16;
+    const char* base = page_base(k_cache, tl, bad);
+    const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + k_lane_off;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      buf[kk] = *reinterpret_cast<const u32x4*>(base + off + 64u * kk);
+  };
+  auto score_tile = [&](int tile, const u32x4 (&buf)[KK], bool bad) {
+    const int tl = tile * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
+                                                    __builtin_bit_cast(bf16x8, buf[kk]), acc, 0,
+                                                    0, 0);
+    // lane (lq, lr) holds S[head 4*lq + i][token tl + lr], i = 0..3
+    if (lq < GQ) {
+      const bool valid = tl + lr < n_s;
+      f32x4 sv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sv[i] = bad ? __builtin_nanf("") : (valid ? acc[i] * score_scale : -INFINITY);
+      *reinterpret_cast<f32x4*>(&s_tile[(tl + lr) * GP + 4 * lq]) = sv;
+    }
+  };
+
+  const int ntile = (n_s + 15) >> 4;
+  const int nk = ntile > wave ? (ntile - 1 - wave) / kWaves + 1 : 0;  // tiles of this wave
+  {
+    // Two register buffers; in the steady state the loads of the next tile are
+    // issued (unconditionally, so the wait counts stay exact) before the
+    // current tile's MFMAs.
+    u32x4 ka[KK], kb[KK];
+    bool bada = false, badb = false;
+    if (nk > 0) load_k(wave, ka, bada);
+    int j = 0;
+    for (; j + 2 < nk; j += 2) {
+      load_k(wave + (j + 1) * kWaves, kb, badb);
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(wave + j * kWaves, ka, bada);
+      load_k(wave + (j + 2) * kWaves, ka, bada);
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(wave + (j + 1) * kWaves, kb, badb);
+    }
+    if (j + 1 < nk) {
+      load_k(wave + (j + 1) * kWaves, kb, badb);
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(wave + j * kWaves, ka, bada);
+      score_tile(wave + (j + 1) * kWaves, kb, badb);
+    } else if (j < nk) {
+      score_tile(wave + j * kWaves, ka, bada);
+    }
+  }
+
+  // ---- V loads of the first P.V step go out before the softmax ------------
+  const int r = lane / LPR;  // token row inside a load instruction
+  const int c = lane % LPR;  // 16-byte chunk of the row: dims 8c .. 8c+7
+  const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 16u * c;
+  auto load_v = [&](int blk, u32x4 (&buf)[PV_U]) {
+    const int tl = blk * BR;
+    bool bad;
+    const char* base = page_base(v_cache, tl, bad);  // bad pages: scores are NaN already
+    const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + v_lane_off;
+#pragma unroll
+    for (int u = 0; u < PV_U; ++u)
+      buf[u] = *reinterpret_cast<const u32x4*>(base + off + (uint32_t)(u * RPI) * row_bytes);
+  };
+  const int nblk = (n_s + BR - 1) / BR;
+  const int nv = nblk > wave ? (nblk - 1 - wave) / kWaves + 1 : 0;  // blocks of this wave
+  u32x4 va[PV_U], vb[PV_U];
+  if (nv > 0) load_v(wave, va);
+  __syncthreads();
+
+  // ---- phase 2: softmax over the split, per head ------------------------
+  {
+    const int nval = ntile * 16 * GP;
+    const int col = threadIdx.x & (GP - 1);  // 256 % GP == 0: fixed column per thread
+    float mx = -INFINITY;
+    for (int e = threadIdx.x; e < nval; e += kThreads) mx = fmaxf(mx, s_tile[e]);
+#pragma unroll
+    for (int off = GP; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane < GP) red[wave * 16 + lane] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[col], red[16 + col]), fmaxf(red[32 + col], red[48 + col]));
+    float sum = 0.f;
+    for (int e = threadIdx.x; e < nval; e += kThreads) {
+      const float p = fast_exp2(s_tile[e] - mx);
+      s_tile[e] = p;
+      sum += p;
+    }
+#pragma unroll
+    for (int off = GP; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
+    if (lane < GP) red[64 + wave * 16 + lane] = sum;
+    __syncthreads();
+    if ((int)threadIdx.x < G) {
+      const float l = (red[64 + col] + red[80 + col]) + (red[96 + col] + red[112 + col]);
+      float* ml = ws_ml + (((size_t)b * num_q_heads + (size_t)h * G + col) * num_splits + s) * 2;
+      ml[0] = mx;
+      ml[1] = l;
+    }
+  }
+
+  // ---- phase 3: acc = P . V on the vector ALUs ----------------------------
+  float acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+
+  auto pv_block = [&](int blk, u32x4 (&buf)[PV_U]) {
+    const int tl = blk * BR;
+    if (tl + BR > n_s) {  // last block: rows past the context may hold NaN
+#pragma unroll
+      for (int u = 0; u < PV_U; ++u)
+        if (tl + u * RPI + r >= n_s) buf[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < PV_U; ++u) {
+      const int t = tl + u * RPI + r;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_lo(buf[u][i]);
+        v[2 * i + 1] = bf16_hi(buf[u][i]);
+      }
+      float p[GP];
+#pragma unroll
+      for (int j = 0; j < GP / 4; ++j) {
+        const f32x4 pj = *reinterpret_cast<const f32x4*>(&s_tile[t * GP + 4 * j]);
+        p[4 * j] = pj[0];
+        p[4 * j + 1] = pj[1];
+        p[4 * j + 2] = pj[2];
+        p[4 * j + 3] = pj[3];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[g], v[e], acc[g][e]);
+    }
+  };
+  {
+    int j = 0;
+    for (; j + 2 < nv; j += 2) {
+      load_v(wave + (j + 1) * kWaves, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block(wave + j * kWaves, va);
+      load_v(wave + (j + 2) * kWaves, va);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block(wave + (j + 1) * kWaves, vb);
+    }
+    if (j + 1 < nv) {
+      load_v(wave + (j + 1) * kWaves, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block(wave + j * kWaves, va);
+      pv_block(wave + (j + 1) * kWaves, vb);
+    } else if (j < nv) {
+      pv_block(wave + j * kWaves, va);
+    }
+  }
+
+  // rows -> one, inside the wave (lanes with the same chunk c)
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+
+  // waves -> one, in LDS, fixed order: (w0 + w2) + (w1 + w3)
+  __syncthreads();  // every wave is done reading the probabilities
+  float* ra = smem;  // [2][G][D]
+  if (r == 0 && wave < 2) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float* dst = &ra[(wave * G + g) * D + 8 * c];
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[g][0], acc[g][1], acc[g][2], acc[g][3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[g][4], acc[g][5], acc[g][6], acc[g][7]};
+    }
+  }
+  __syncthreads();
+  if (r == 0 && wave >= 2) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float* dst = &ra[((wave - 2) * G + g) * D + 8 * c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] += acc[g][e];
+    }
+  }
+  __syncthreads();
+  float* dst = ws_acc + (((size_t)b * num_q_heads + (size_t)h * G) * num_splits + s) * D;
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int g = i / D;
+    const int d = i - g * D;
+    dst[(size_t)g * num_splits * D + d] = ra[i] + ra[G * D + i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void reduce_kernel(const float* __restrict__ ws_acc,
+                                                   const float* __restrict__ ws_ml,
+                                                   const int32_t* __restrict__ context_lens,
+                                                   uint16_t* __restrict__ out, int num_q_heads,
+                                                   int num_splits, int split_tokens, int max_ctx) {
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const int ctx = context_lens[b];
+  const size_t row = (size_t)b * num_q_heads + hq;
+  float o;
+  if (ctx < 0 || ctx > max_ctx) {
+    o = __builtin_nanf("");  // caller error, made visible
+  } else {
+    const int nv = (ctx + split_tokens - 1) / split_tokens;  // splits that hold tokens
+    const float* ml = ws_ml + row * num_splits * 2;
+    const float* acc = ws_acc + row * num_splits * D + d;
+    float m = -INFINITY;
+    for (int s = 0; s < nv; ++s) m = fmaxf(m, ml[2 * s]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nv; ++s) {
+      const float w = fast_exp2(ml[2 * s] - m);
+      num = fmaf(w, acc[(size_t)s * D], num);
+      den = fmaf(w, ml[2 * s + 1], den);
+    }
+    o = nv > 0 ? num / den : 0.f;  // empty context: exact zeros
+  }
+  out[row * D + d] = f32_to_bf16(o);
+}
+
+template <int D, int G>
+int launch_partition_dg(const LaunchArgs& a) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
+  const dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  const size_t lds = sizeof(float) * lds_words<D, G>(a.split_pages);
+  void* args[] = {(void*)&a.q,           (void*)&a.k_cache,      (void*)&a.v_cache,
+                  (void*)&a.block_table, (void*)&a.context_lens, (void*)&a.ws_acc,
+                  (void*)&a.ws_ml,       (void*)&a.num_kv_heads, (void*)&a.max_pages,
+                  (void*)&a.num_pages,   (void*)&a.split_pages,  (void*)&a.num_splits,
+                  (void*)&a.score_scale};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G>), grid,
+                              dim3(kThreads), args, lds, stream);
+}
+
+template <int D>
+int launch_reduce_d(const LaunchArgs& a) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
+  const int split_tokens = a.split_pages * kPage;
+  const int max_ctx = a.max_pages * kPage;
+  void* args[] = {(void*)&a.ws_acc,     (void*)&a.ws_ml,       (void*)&a.context_lens,
+                  (void*)&a.out,        (void*)&a.num_q_heads, (void*)&a.num_splits,
+                  (void*)&split_tokens, (void*)&max_ctx};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel<D>),
+                              dim3(a.num_q_heads, a.batch), dim3(D), args, 0, stream);
+}
+
+typedef int (*LaunchFn)(const LaunchArgs&);
+
+#define PA_G_LIST(D)                                                                   \
+  {nullptr,                      &launch_partition_dg<D, 1>,  &launch_partition_dg<D, 2>, \
+   &launch_partition_dg<D, 3>,   &launch_partition_dg<D, 4>,  &launch_partition_dg<D, 5>, \
+   &launch_partition_dg<D, 6>,   &launch_partition_dg<D, 7>,  &launch_partition_dg<D, 8>, \
+   &launch_partition_dg<D, 9>,   &launch_partition_dg<D, 10>, &launch_partition_dg<D, 11>, \
+   &launch_partition_dg<D, 12>,  &launch_partition_dg<D, 13>, &launch_partition_dg<D, 14>, \
+   &launch_partition_dg<D, 15>,  &launch_partition_dg<D, 16>}
+
+const LaunchFn kPartition128[17] = PA_G_LIST(128);
+const LaunchFn kPartition256[17] = PA_G_LIST(256);
+
+template <int D>
+size_t lds_bytes_for(int g, int split_pages) {
+  switch (g) {
+#define PA_LDS_CASE(G) \
+  case G:              \
+    return sizeof(float) * lds_words<D, G>(split_pages);
+    PA_LDS_CASE(1) PA_LDS_CASE(2) PA_LDS_CASE(3) PA_LDS_CASE(4) PA_LDS_CASE(5) PA_LDS_CASE(6)
+    PA_LDS_CASE(7) PA_LDS_CASE(8) PA_LDS_CASE(9) PA_LDS_CASE(10) PA_LDS_CASE(11)
+    PA_LDS_CASE(12) PA_LDS_CASE(13) PA_LDS_CASE(14) PA_LDS_CASE(15) PA_LDS_CASE(16)
+#undef PA_LDS_CASE
+    default:
+      return 0;
+  }
+}
+
+}  // namespace
+
+bool has_kernels(int head_dim, int gqa_ratio) {
+  return (head_dim == 128 || head_dim == 256) && gqa_ratio >= 1 && gqa_ratio <= 16;
+}
+
+size_t partition_lds_bytes(int head_dim, int gqa_ratio, int split_pages) {
+  if (!has_kernels(head_dim, gqa_ratio)) return 0;
+  return head_dim == 128 ? lds_bytes_for<128>(gqa_ratio, split_pages)
+                         : lds_bytes_for<256>(gqa_ratio, split_pages);
+}
+
+int launch_partition(const LaunchArgs& a) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  return (a.head_dim == 128 ? kPartition128[g] : kPartition256[g])(a);
+}
+
+int launch_reduce(const LaunchArgs& a) {
+  return a.head_dim == 128 ? launch_reduce_d<128>(a) : launch_reduce_d<256>(a);
+}
+
+}  // namespace pa

@@ -1,0 +1,38 @@
+// Internal interface between the C-ABI host code (api.cpp) and the kernel
+// launchers (decode_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything the two kernels need for one call, already validated on the host.
+struct LaunchArgs {
+  const uint16_t* q;          // bf16 [B, Hq, D]
+  const uint16_t* k_cache;    // bf16 [N, P, Hkv, D]
+  const uint16_t* v_cache;    // bf16 [N, P, Hkv, D]
+  const int32_t* block_table; // int32 [B, W]
+  const int32_t* context_lens;// int32 [B]
+  uint16_t* out;              // bf16 [B, Hq, D]
+  float* ws_acc;              // f32 [B, Hq, S, D]   unnormalised split outputs
+  float* ws_ml;               // f32 [B, Hq, S, 2]   (max, sum) per split, log2 units
+  int batch, num_q_heads, num_kv_heads, head_dim, max_pages, num_pages;
+  int split_pages, num_splits;
+  float score_scale;          // scale * log2(e), applied to q.k in FP32
+  void* stream;               // hipStream_t
+};
+
+// True if a kernel pair is compiled for (head_dim, gqa_ratio).
+bool has_kernels(int head_dim, int gqa_ratio);
+
+// Bytes of dynamic LDS the partition kernel uses for one split.
+size_t partition_lds_bytes(int head_dim, int gqa_ratio, int split_pages);
+
+// Enqueue the partition kernel (split partials -> workspace) or the reduce
+// kernel (workspace -> out). Return 0 on success, else the HIP error code of
+// the failed launch.
+int launch_partition(const LaunchArgs& a);
+int launch_reduce(const LaunchArgs& a);
+
+}  // namespace pa

@@ -1,0 +1,238 @@
+"""Python binding of libpagedattn (paged GQA decode attention on MI355X).
+
+This module only marshals arguments: it checks tensor dtypes, devices, shapes
+and contiguity on host metadata, fills the C ``pa_shape_t`` and calls the C
+ABI declared in ``include/pagedattn.h`` through ctypes, on torch's current
+stream. Every step of the computation runs in the library's HIP kernels; if
+the library is missing, importing the binding raises instead of falling back.
+
+Names follow the C ABI: ``pa_decode``, ``pa_plan``, ``pa_workspace_size``,
+``pa_status_string``, ``pa_abi_version``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_NULL_POINTER = 1
+PA_ERR_INVALID_ARGUMENT = 2
+PA_ERR_UNSUPPORTED = 3
+PA_ERR_WORKSPACE_TOO_SMALL = 4
+PA_ERR_LAUNCH = 5
+PAGE_SIZE = 128
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("split_pages", ctypes.c_int32),
+    ]
+
+
+class PaPlan(ctypes.Structure):
+    _fields_ = [
+        ("split_pages", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pa_status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m paged_gqa_attention_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.pa_abi_version.restype = ctypes.c_int
+    lib.pa_abi_version.argtypes = []
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_plan.restype = ctypes.c_int
+    lib.pa_plan.argtypes = [ctypes.POINTER(PaShape), ctypes.POINTER(PaPlan)]
+    lib.pa_workspace_size.restype = ctypes.c_int
+    lib.pa_workspace_size.argtypes = [ctypes.POINTER(PaShape), ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [
+        ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    lib.pa_decode_partials.restype = ctypes.c_int
+    lib.pa_decode_partials.argtypes = [
+        ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p,
+    ]
+    lib.pa_merge_partials.restype = ctypes.c_int
+    lib.pa_merge_partials.argtypes = [
+        ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    return lib
+
+
+_lib = _load()
+lib = _lib  # the raw ctypes handle, for tests that call the C ABI with raw pointers
+
+
+def pa_abi_version() -> int:
+    return int(_lib.pa_abi_version())
+
+
+def pa_status_string(status: int) -> str:
+    return _lib.pa_status_string(int(status)).decode()
+
+
+def make_shape(batch, num_q_heads, num_kv_heads, head_dim, max_pages_per_seq, num_pages,
+               page_size=PAGE_SIZE, split_pages=0) -> PaShape:
+    return PaShape(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                   int(page_size), int(max_pages_per_seq), int(num_pages), int(split_pages))
+
+
+def pa_plan(shape: PaShape) -> PaPlan:
+    plan = PaPlan()
+    st = _lib.pa_plan(ctypes.byref(shape), ctypes.byref(plan))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_plan")
+    return plan
+
+
+def pa_workspace_size(shape: PaShape) -> int:
+    n = ctypes.c_size_t(0)
+    st = _lib.pa_workspace_size(ctypes.byref(shape), ctypes.byref(n))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_workspace_size")
+    return int(n.value)
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A cached device workspace of at least ``nbytes`` (256-byte aligned)."""
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def shape_of(q, k_cache, block_table, split_pages: int = 0) -> PaShape:
+    B, Hq, D = q.shape
+    N, P, Hkv, Dk = k_cache.shape
+    return make_shape(B, Hq, Hkv, D, block_table.shape[1], N, P, split_pages)
+
+
+def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Hq,D] and k_cache == v_cache shape [N,P,Hkv,D]")
+    B, Hq, D = q.shape
+    if k_cache.shape[3] != D:
+        raise ValueError("head_dim of q and of the caches differ")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("expected block_table [B, W] and context_lens [B]")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, torch.bfloat16),
+                        ("v_cache", v_cache, torch.bfloat16),
+                        ("block_table", block_table, torch.int32),
+                        ("context_lens", context_lens, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU of q")
+
+
+def _check_out(out, q):
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              block_table: torch.Tensor, context_lens: torch.Tensor,
+              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+              split_pages: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention over a paged BF16 cache; returns ``out`` [B, Hq, D] BF16.
+
+    q [B, Hq, D] bf16; k_cache, v_cache [N, 128, Hkv, D] bf16; block_table
+    [B, W] int32; context_lens [B] int32; all contiguous on one GPU.
+    ``scale`` defaults to 1/sqrt(D). ``split_pages`` = 0 lets the library plan.
+    Runs on torch's current stream.
+    """
+    _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    shape = shape_of(q, k_cache, block_table, split_pages)
+    if shape.batch == 0:
+        return out
+    need = pa_workspace_size(shape)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    st = _lib.pa_decode(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
+                        v_cache.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
+                        ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_decode")
+    return out
+
+
+def pa_decode_partials(q, k_cache, v_cache, block_table, context_lens, workspace,
+                       scale: Optional[float] = None, split_pages: int = 0) -> None:
+    """Stage 1 of pa_decode: write the split partials into ``workspace``."""
+    _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    shape = shape_of(q, k_cache, block_table, split_pages)
+    st = _lib.pa_decode_partials(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
+                                 v_cache.data_ptr(), block_table.data_ptr(),
+                                 context_lens.data_ptr(), ctypes.c_float(scale),
+                                 workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(q.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_decode_partials")
+
+
+def pa_merge_partials(shape: PaShape, context_lens: torch.Tensor, workspace: torch.Tensor,
+                      out: torch.Tensor) -> torch.Tensor:
+    """Stage 2 of pa_decode: merge the partials in ``workspace`` into ``out``."""
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise TypeError("context_lens must be contiguous int32")
+    st = _lib.pa_merge_partials(ctypes.byref(shape), context_lens.data_ptr(),
+                                workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), out.data_ptr(),
+                                _stream(out.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_merge_partials")
+    return out

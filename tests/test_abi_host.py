@@ -1,0 +1,177 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, plans splits without device data, and rejects bad arguments
+with status codes before launching anything. No GPU is needed: every pa_decode
+call here fails validation on the host before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+pa = pytest.importorskip("paged_gqa_attention_amd.pagedattn",
+                         reason="libpagedattn.so not built (run __graft_entry__.build())")
+
+import torch  # noqa: E402
+
+# Tests that hand fake device addresses to pa_decode only run where no GPU is
+# visible: validation rejects them on the host, and if it ever did not, there
+# is no device to launch on.
+fake_pointers = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                   reason="passes fake device pointers; host-only check")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert names == ["pa_abi_version", "pa_decode", "pa_decode_partials", "pa_merge_partials",
+                     "pa_plan", "pa_status_string", "pa_workspace_size"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_constants_match_header():
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define PA_ABI_VERSION (\d+)", text).group(1))
+    assert pa.pa_abi_version() == ver
+    assert int(re.search(r"#define PA_PAGE_SIZE (\d+)", text).group(1)) == pa.PAGE_SIZE
+    codes = dict(re.findall(r"(PA_(?:OK|ERR_[A-Z_]+)) = (\d+)", text))
+    for k, v in codes.items():
+        assert getattr(pa, k) == int(v)
+
+
+def test_status_strings():
+    for code in range(6):
+        s = pa.pa_status_string(code)
+        assert s.startswith("PA_")
+    assert "unknown" in pa.pa_status_string(99)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(pa.PaShape) == 8 * 4
+    assert ctypes.sizeof(pa.PaPlan) == 16
+
+
+@pytest.mark.parametrize("cfg,expect", [
+    ((2, 40, 8, 128, 2, 4), (1, 2)),       # B=2, W=2: one page per split
+    ((16, 40, 8, 128, 32, 512), (4, 8)),   # 128 (seq, kv head) pairs -> 8 splits of 512 tokens
+    ((256, 40, 8, 128, 32, 2050), (4, 8)),
+    ((32, 16, 2, 256, 32, 1024), (2, 16)), # 64 pairs -> 16 splits of 256 tokens
+])
+def test_plan_for_the_standard_workloads(cfg, expect):
+    plan = pa.pa_plan(pa.make_shape(*cfg))
+    assert (plan.split_pages, plan.num_splits) == expect
+    B, Hq, Hkv, D, W, N = cfg
+    rows = B * Hq * plan.num_splits
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert plan.workspace_bytes == r256(rows * D * 4) + r256(rows * 2 * 4)
+    assert pa.pa_workspace_size(pa.make_shape(*cfg)) == plan.workspace_bytes
+
+
+def test_plan_explicit_split_pages_and_clamp():
+    for sp in (1, 2, 3, 7, 15):
+        plan = pa.pa_plan(pa.make_shape(4, 40, 8, 128, 32, 200, split_pages=sp))
+        assert plan.split_pages == sp
+        assert plan.num_splits == -(-32 // sp)
+    # a split whose score tile would exceed 64 KiB of LDS is clamped
+    plan = pa.pa_plan(pa.make_shape(4, 40, 8, 128, 32, 200, split_pages=32))
+    assert 1 <= plan.split_pages < 32
+    plan = pa.pa_plan(pa.make_shape(4, 4, 4, 128, 2, 20, split_pages=9))
+    assert plan.split_pages == 2
+
+
+@fake_pointers
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", -1, 2), ("num_q_heads", 0, 2), ("num_kv_heads", 0, 2), ("num_q_heads", 41, 2),
+    ("head_dim", 64, 3), ("head_dim", 0, 2), ("page_size", 64, 3), ("page_size", 0, 2),
+    ("max_pages_per_seq", 0, 2), ("num_pages", 0, 2), ("split_pages", -1, 2),
+    ("num_q_heads", 8 * 17, 3),  # GQA ratio 17
+    ("batch", 70000, 3),
+])
+def test_invalid_shapes(field, value, code):
+    s = pa.make_shape(2, 40, 8, 128, 32, 64)
+    setattr(s, field, value)
+    plan = pa.PaPlan()
+    assert pa.lib.pa_plan(ctypes.byref(s), ctypes.byref(plan)) == code
+    n = ctypes.c_size_t()
+    assert pa.lib.pa_workspace_size(ctypes.byref(s), ctypes.byref(n)) == code
+    dummy = 1 << 20
+    assert pa.lib.pa_decode(ctypes.byref(s), dummy, dummy, dummy, dummy, dummy,
+                            ctypes.c_float(0.1), dummy, dummy, 1 << 30, None) == code
+    assert pa.lib.pa_decode_partials(ctypes.byref(s), dummy, dummy, dummy, dummy, dummy,
+                                     ctypes.c_float(0.1), dummy, 1 << 30, None) == code
+    assert pa.lib.pa_merge_partials(ctypes.byref(s), dummy, dummy, 1 << 30, dummy, None) == code
+
+
+def test_every_supported_ratio_plans():
+    for D in (128, 256):
+        for g in range(1, 17):
+            plan = pa.pa_plan(pa.make_shape(3, 2 * g, 2, D, 32, 100))
+            assert plan.num_splits >= 1
+
+
+@fake_pointers
+def test_null_pointers():
+    s = pa.make_shape(2, 40, 8, 128, 32, 64)
+    assert pa.lib.pa_plan(None, ctypes.byref(pa.PaPlan())) == pa.PA_ERR_NULL_POINTER
+    assert pa.lib.pa_plan(ctypes.byref(s), None) == pa.PA_ERR_NULL_POINTER
+    assert pa.lib.pa_workspace_size(ctypes.byref(s), None) == pa.PA_ERR_NULL_POINTER
+    d = 1 << 20
+    args = [d, d, d, d, d, ctypes.c_float(0.1), d, d, 1 << 30, None]
+    for i in (0, 1, 2, 3, 4, 6, 7):
+        a = list(args)
+        a[i] = None
+        assert pa.lib.pa_decode(ctypes.byref(s), *a) == pa.PA_ERR_NULL_POINTER, i
+    assert pa.lib.pa_decode(None, *args) == pa.PA_ERR_NULL_POINTER
+    # stage entry points: partials needs no `out`, merge needs no q/K/V/table
+    pargs = [d, d, d, d, d, ctypes.c_float(0.1), d, 1 << 30, None]
+    for i in (0, 1, 2, 3, 4, 6):
+        a = list(pargs)
+        a[i] = None
+        assert pa.lib.pa_decode_partials(ctypes.byref(s), *a) == pa.PA_ERR_NULL_POINTER, i
+    margs = [d, d, 1 << 30, d, None]
+    for i in (0, 1, 3):
+        a = list(margs)
+        a[i] = None
+        assert pa.lib.pa_merge_partials(ctypes.byref(s), *a) == pa.PA_ERR_NULL_POINTER, i
+
+
+def test_batch_zero_is_a_no_op():
+    s = pa.make_shape(0, 40, 8, 128, 32, 64)
+    assert pa.lib.pa_decode(ctypes.byref(s), None, None, None, None, None,
+                            ctypes.c_float(0.1), None, None, 0, None) == pa.PA_OK
+
+
+@fake_pointers
+def test_misaligned_pointers_scale_and_workspace():
+    s = pa.make_shape(2, 40, 8, 128, 32, 64)
+    ws = pa.pa_workspace_size(s)
+    d = 1 << 20
+    ok = [d, d, d, d, d, ctypes.c_float(0.1), d, d, ws, None]
+    for i, bad in ((0, d + 2), (1, d + 8), (2, d + 4), (6, d + 2), (3, d + 2), (4, d + 1)):
+        a = list(ok)
+        a[i] = bad
+        assert pa.lib.pa_decode(ctypes.byref(s), *a) == pa.PA_ERR_INVALID_ARGUMENT, i
+    for sc in (float("nan"), float("inf"), -float("inf")):
+        a = list(ok)
+        a[5] = ctypes.c_float(sc)
+        assert pa.lib.pa_decode(ctypes.byref(s), *a) == pa.PA_ERR_INVALID_ARGUMENT
+    a = list(ok)
+    a[7] = d + 128                      # workspace must be 256-byte aligned
+    assert pa.lib.pa_decode(ctypes.byref(s), *a) == pa.PA_ERR_INVALID_ARGUMENT
+    a = list(ok)
+    a[8] = ws - 1
+    assert pa.lib.pa_decode(ctypes.byref(s), *a) == pa.PA_ERR_WORKSPACE_TOO_SMALL
