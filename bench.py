@@ -54,7 +54,61 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                         "WRITE_SIZE, both with --calibrate-copy) into the traffic file; no GPU")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def _counter_rows(d, counter):
+    """(kernel name, grid size, value) per dispatch from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    rows = []
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                grid = r.get("Grid_Size") or r.get("Grid_Size_X") or "0"
+                rows.append((r["Kernel_Name"], int(float(grid)), float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per partition-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB).
+
+    Each counter is scaled by what it reads for the 1 GiB device copy of the
+    same run (1 GiB read, 1 GiB written), so the result is in true bytes.
+    """
+    import statistics
+    out = {"kernel": "partition_kernel<128, 5>", "workload": "batch 16 x 4096, 40/8 heads, D 128",
+           "kernel_source_sha256_16": kernel_source_hash()}
+    per = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, name)
+        part = [v for k, g, v in rows if "partition_kernel<128, 5>" in k]
+        copy = [v for k, g, v in rows if "copy" in k.lower() and "partition" not in k
+                and "reduce" not in k]
+        if not part or not copy:
+            raise SystemExit(f"{name}: partition or copy dispatches missing in {d}")
+        copy_kib = max(copy)                     # the 1 GiB copy is the largest copy dispatch
+        scale = (COPY_BYTES / 1024.0) / copy_kib
+        per[name] = {"partition_kib_per_dispatch_median": statistics.median(part),
+                     "dispatches": len(part), "copy_kib": copy_kib, "scale": scale,
+                     "bytes_per_launch": statistics.median(part) * 1024.0 * scale}
+    out["counters"] = per
+    out["hbm_bytes_per_launch"] = round(per["FETCH_SIZE"]["bytes_per_launch"] +
+                                        per["WRITE_SIZE"]["bytes_per_launch"])
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 class Decoder:
@@ -118,9 +172,12 @@ def cpu_model() -> str:
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence, KV head or page range; see the design notes)",
+              "(across GPUs the decode path would shard by sequence, KV head or page range)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -284,12 +341,12 @@ def main():
         result["other_workloads"] = extra
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = 1 << 30
+        result["calibration_copy_bytes"] = COPY_BYTES
 
     print(json.dumps(result), flush=True)
 

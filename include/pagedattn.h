@@ -112,10 +112,13 @@ const char* pa_status_string(int status);
 pa_status_t pa_plan(const pa_shape_t* shape, pa_plan_t* plan);
 
 /* Bytes of device workspace pa_decode needs for `shape` (FP32 split partials:
- * unnormalised output rows and the running max / sum per split). */
+ * unnormalised output rows and the running max / sum per split). Its contents
+ * between calls do not matter; it needs no initialisation. */
 pa_status_t pa_workspace_size(const pa_shape_t* shape, size_t* bytes);
 
-/* Enqueue decode attention on `stream`.
+/* Enqueue decode attention on `stream`: the partition kernel writes every
+ * split's partials to the workspace, then the merge kernel combines them (the
+ * log-sum-exp combination described below) and writes `out`.
  *   q            device, BF16 [B, Hq, D], 16-byte aligned
  *   k_cache      device, BF16 [N, P, Hkv, D], 16-byte aligned
  *   v_cache      device, BF16 [N, P, Hkv, D], 16-byte aligned (may equal k_cache)
@@ -134,7 +137,8 @@ pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cach
 
 /* The two stages of pa_decode, for callers that move or combine split partials
  * themselves (for instance a context-parallel decode that gives each GPU a
- * range of pages and merges the partials after exchanging them).
+ * range of pages and merges the partials after exchanging them). Together
+ * they produce the same bits as pa_decode.
  *
  * Workspace layout (FP32), with S = plan.num_splits and T = page_size *
  * plan.split_pages: split s covers tokens [s*T, (s+1)*T) of a sequence, and

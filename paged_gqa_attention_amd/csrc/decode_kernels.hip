@@ -24,8 +24,8 @@
 //      dims, then rows and waves are summed in a fixed order.
 //   The unnormalised output, the max and the sum of each split go to an FP32
 //   workspace.
-//   reduce_kernel<D>: one workgroup per (query head, sequence) merges the
-//   splits that cover the context: M = max m_s, out = sum 2^(m_s-M) acc_s /
+//   reduce_kernel<D>: merges, for every (sequence, query head), the splits that
+//   cover the context: M = max m_s, out = sum 2^(m_s-M) acc_s /
 //   sum 2^(m_s-M) l_s, rounded to BF16 (nearest even).
 //
 // Nothing here uses atomics; the reduction order is fixed, so repeated calls
@@ -43,6 +43,8 @@ namespace {
 constexpr int kPage = 128;      // tokens per page
 constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
+constexpr int kKSlots = 2;      // register slots of the K pipeline
+constexpr int kVSlots = 2;      // register slots of the V pipeline
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +67,94 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Software pipeline over n items held in NB register slots (item i in slot
+// i % NB): items i+1 .. i+NB-1 are loading while item i is used. In the steady
+// state every prefetch is issued unconditionally and pinned before the use
+// with a scheduling barrier, so the compiler's wait counts let exactly the
+// consumed item's loads complete; the tail (< 2*NB-1 items) guards each one.
+// `load(item, slot)` and `use(item, slot)` receive compile-time slot indices
+// after unrolling.
+template <int NB, class Load, class Use>
+__device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i)
+    if (i < n) load(i, i);
+  int j = 0;
+  for (; j + 2 * NB - 2 < n; j += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      load(j + u + NB - 1, (u + NB - 1) % NB);
+      __builtin_amdgcn_sched_barrier(0);
+      use(j + u, u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * NB - 2; ++u) {
+    if (j + u < n) {
+      if (j + u + NB - 1 < n) load(j + u + NB - 1, (u + NB - 1) % NB);
+      use(j + u, u % NB);
+    }
+  }
+}
+
+// Log-sum-exp merge of the first nv split partials of one (sequence, query
+// head) row, for the 4 dims d4 .. d4+3: M = max m_s, out = sum 2^(m_s-M) acc_s
+// / sum 2^(m_s-M) l_s. The partials of up to kMergeChunk splits are loaded
+// together, then folded into a running state, so a row costs one memory round
+// trip for the usual split counts. nv == 0 (empty context) gives zeros.
+constexpr int kMergeChunk = 8;
+
+template <int D>
+__device__ __forceinline__ f32x4 merge_row(const float* __restrict__ ws_acc,
+                                           const float* __restrict__ ws_ml, size_t row,
+                                           int num_splits, int nv, int d4) {
+  const float* ml = ws_ml + row * num_splits * 2;
+  const float* acc = ws_acc + row * num_splits * D + d4;
+  float m_run = -INFINITY, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nv; s0 += kMergeChunk) {
+    float2 mlv[kMergeChunk];
+    f32x4 av[kMergeChunk];
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      if (s0 + i < nv) {
+        mlv[i] = *reinterpret_cast<const float2*>(ml + 2 * (s0 + i));
+        av[i] = *reinterpret_cast<const f32x4*>(acc + (size_t)(s0 + i) * D);
+      }
+    }
+    float mc = m_run;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+      if (s0 + i < nv) mc = fmaxf(mc, mlv[i].x);
+    const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mc);
+    den *= a;
+    num *= a;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      if (s0 + i < nv) {
+        const float w = fast_exp2(mlv[i].x - mc);
+        den = fmaf(w, mlv[i].y, den);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] = fmaf(w, av[i][e], num[e]);
+      }
+    }
+    m_run = mc;
+  }
+  f32x4 res = {0.f, 0.f, 0.f, 0.f};
+  if (nv > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = num[e] / den;
+  }
+  return res;
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 v) {
+  uint2 packed;
+  packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = packed;
+}
 
 // Score row stride in LDS: G padded to a power of two >= 4, so that one
 // 16-byte store per MFMA lane group lands a whole group of 4 heads.
@@ -106,20 +196,23 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   constexpr int RPI = 64 / LPR;           // token rows per load instruction in P.V
   constexpr int PV_U = 4;                 // load instructions per P.V block
   constexpr int BR = RPI * PV_U;          // token rows per P.V block (16 or 8)
+  constexpr int KNB = kKSlots;            // K tiles in registers (KNB-1 in flight)
+  constexpr int VNB = kVSlots;            // V blocks in registers (VNB-1 in flight)
   static_assert(16 % BR == 0, "P.V blocks must tile the 16-token score tiles");
 
   extern __shared__ float smem[];
 
-  const int s = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // 1-D grid, (sequence, KV head) pair fastest: consecutive workgroups land on
+  // different XCDs (dispatch is round-robin over the 8 XCDs), so every XCD gets
+  // an even share of every split index, and the first split of every pair,
+  // which always holds tokens, is dispatched first.
+  const int num_pairs = gridDim.x / num_splits;
+  const int pair = blockIdx.x % num_pairs;
+  const int s = blockIdx.x / num_pairs;
+  const int h = pair % num_kv_heads;
+  const int b = pair / num_kv_heads;
   const int num_q_heads = num_kv_heads * G;
   const int split_tokens = split_pages * kPage;
-  int ctx = context_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
-  const int t0 = s * split_tokens;  // first token of this split
-  const int n_s = min(ctx - t0, split_tokens);
-  if (n_s <= 0) return;  // split past the context: nothing to write
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -130,13 +223,13 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   float* red = smem + lds_tile_words<D, G>(split_pages);       // [2][4][16]
   int* s_page = reinterpret_cast<int*>(red + kRedWords);       // [split_pages]
 
-  // Page ids this split needs, read once; an id outside the pool becomes -1.
-  const int npg = (n_s + kPage - 1) / kPage;
-  if ((int)threadIdx.x < npg) {
-    const int page = block_table[(size_t)b * max_pages + (size_t)s * split_pages + threadIdx.x];
-    s_page[threadIdx.x] = (unsigned)page < (unsigned)num_pages ? page : -1;
-  }
-
+  // The page ids of the split and q do not depend on the context length, so
+  // their loads go out together with it (one memory round trip, not three).
+  // Entries past the context are read but never used.
+  const int first_page = s * split_pages;
+  int page_id = -1;
+  if ((int)threadIdx.x < split_pages && first_page + (int)threadIdx.x < max_pages)
+    page_id = block_table[(size_t)b * max_pages + first_page + threadIdx.x];
   // A operand of the score MFMA: lane (lq, lr) holds q[head lr][32*kk + 8*lq .. +7]
   // (zero rows for heads >= G).
   u32x4 qa[KK];
@@ -146,6 +239,16 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     for (int kk = 0; kk < KK; ++kk)
       qa[kk] = (lr < G) ? load16(qrow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
   }
+  int ctx = context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
+  const int t0 = s * split_tokens;  // first token of this split
+  const int n_s = min(ctx - t0, split_tokens);
+  if (n_s <= 0) return;  // split past the context: nothing to write
+
+  // Page ids this split needs; an id outside the pool becomes -1.
+  const int npg = (n_s + kPage - 1) / kPage;
+  if ((int)threadIdx.x < npg)
+    s_page[threadIdx.x] = (unsigned)page_id < (unsigned)num_pages ? page_id : -1;
   __syncthreads();
 
   const size_t page_bytes = (size_t)kPage * num_kv_heads * D * sizeof(uint16_t);
@@ -193,29 +296,11 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const int ntile = (n_s + 15) >> 4;
   const int nk = ntile > wave ? (ntile - 1 - wave) / kWaves + 1 : 0;  // tiles of this wave
   {
-    // Two register buffers; in the steady state the loads of the next tile are
-    // issued (unconditionally, so the wait counts stay exact) before the
-    // current tile's MFMAs.
-    u32x4 ka[KK], kb[KK];
-    bool bada = false, badb = false;
-    if (nk > 0) load_k(wave, ka, bada);
-    int j = 0;
-    for (; j + 2 < nk; j += 2) {
-      load_k(wave + (j + 1) * kWaves, kb, badb);
-      __builtin_amdgcn_sched_barrier(0);
-      score_tile(wave + j * kWaves, ka, bada);
-      load_k(wave + (j + 2) * kWaves, ka, bada);
-      __builtin_amdgcn_sched_barrier(0);
-      score_tile(wave + (j + 1) * kWaves, kb, badb);
-    }
-    if (j + 1 < nk) {
-      load_k(wave + (j + 1) * kWaves, kb, badb);
-      __builtin_amdgcn_sched_barrier(0);
-      score_tile(wave + j * kWaves, ka, bada);
-      score_tile(wave + (j + 1) * kWaves, kb, badb);
-    } else if (j < nk) {
-      score_tile(wave + j * kWaves, ka, bada);
-    }
+    u32x4 kbuf[KNB][KK];
+    bool kbad[KNB];
+    pipeline<KNB>(
+        nk, [&](int i, int slot) { load_k(wave + i * kWaves, kbuf[slot], kbad[slot]); },
+        [&](int i, int slot) { score_tile(wave + i * kWaves, kbuf[slot], kbad[slot]); });
   }
 
   // ---- V loads of the first P.V step go out before the softmax ------------
@@ -233,8 +318,10 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   };
   const int nblk = (n_s + BR - 1) / BR;
   const int nv = nblk > wave ? (nblk - 1 - wave) / kWaves + 1 : 0;  // blocks of this wave
-  u32x4 va[PV_U], vb[PV_U];
-  if (nv > 0) load_v(wave, va);
+  u32x4 vbuf[VNB][PV_U];
+#pragma unroll
+  for (int i = 0; i < VNB - 1; ++i)
+    if (i < nv) load_v(wave + i * kWaves, vbuf[i]);
   __syncthreads();
 
   // ---- phase 2: softmax over the split, per head ------------------------
@@ -289,9 +376,9 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
         v[2 * i] = bf16_lo(buf[u][i]);
         v[2 * i + 1] = bf16_hi(buf[u][i]);
       }
-      float p[GP];
+      float p[G];
 #pragma unroll
-      for (int j = 0; j < GP / 4; ++j) {
+      for (int j = 0; j < G / 4; ++j) {
         const f32x4 pj = *reinterpret_cast<const f32x4*>(&s_tile[t * GP + 4 * j]);
         p[4 * j] = pj[0];
         p[4 * j + 1] = pj[1];
@@ -299,30 +386,17 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
         p[4 * j + 3] = pj[3];
       }
 #pragma unroll
+      for (int j = (G / 4) * 4; j < G; ++j) p[j] = s_tile[t * GP + j];
+#pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[g], v[e], acc[g][e]);
     }
   };
-  {
-    int j = 0;
-    for (; j + 2 < nv; j += 2) {
-      load_v(wave + (j + 1) * kWaves, vb);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_block(wave + j * kWaves, va);
-      load_v(wave + (j + 2) * kWaves, va);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_block(wave + (j + 1) * kWaves, vb);
-    }
-    if (j + 1 < nv) {
-      load_v(wave + (j + 1) * kWaves, vb);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_block(wave + j * kWaves, va);
-      pv_block(wave + (j + 1) * kWaves, vb);
-    } else if (j < nv) {
-      pv_block(wave + j * kWaves, va);
-    }
-  }
+  // the first VNB-1 blocks were issued before the softmax
+  pipeline<VNB>(
+      nv, [&](int i, int slot) { if (i >= VNB - 1) load_v(wave + i * kWaves, vbuf[slot]); },
+      [&](int i, int slot) { pv_block(wave + i * kWaves, vbuf[slot]); });
 
   // rows -> one, inside the wave (lanes with the same chunk c)
 #pragma unroll
@@ -361,41 +435,34 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   }
 }
 
+// Merge kernel: one 256-thread workgroup merges RPW (sequence, query head)
+// rows; each thread owns 4 consecutive dims of one row.
 template <int D>
-__global__ __launch_bounds__(D) void reduce_kernel(const float* __restrict__ ws_acc,
-                                                   const float* __restrict__ ws_ml,
-                                                   const int32_t* __restrict__ context_lens,
-                                                   uint16_t* __restrict__ out, int num_q_heads,
-                                                   int num_splits, int split_tokens, int max_ctx) {
-  const int hq = blockIdx.x;
-  const int b = blockIdx.y;
-  const int d = threadIdx.x;
-  const int ctx = context_lens[b];
-  const size_t row = (size_t)b * num_q_heads + hq;
-  float o;
+__global__ __launch_bounds__(kThreads) void reduce_kernel(
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
+    const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out, int rows,
+    int num_q_heads, int num_splits, int split_tokens, int max_ctx) {
+  constexpr int TPR = D / 4;             // threads per row
+  constexpr int RPW = kThreads / TPR;    // rows per workgroup (8 or 4)
+  const int row = blockIdx.x * RPW + (int)threadIdx.x / TPR;
+  if (row >= rows) return;
+  const int d4 = ((int)threadIdx.x % TPR) * 4;
+  const int ctx = context_lens[row / num_q_heads];
+  f32x4 res;
   if (ctx < 0 || ctx > max_ctx) {
-    o = __builtin_nanf("");  // caller error, made visible
+    const float nan = __builtin_nanf("");  // caller error, made visible
+    res = f32x4{nan, nan, nan, nan};
   } else {
-    const int nv = (ctx + split_tokens - 1) / split_tokens;  // splits that hold tokens
-    const float* ml = ws_ml + row * num_splits * 2;
-    const float* acc = ws_acc + row * num_splits * D + d;
-    float m = -INFINITY;
-    for (int s = 0; s < nv; ++s) m = fmaxf(m, ml[2 * s]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nv; ++s) {
-      const float w = fast_exp2(ml[2 * s] - m);
-      num = fmaf(w, acc[(size_t)s * D], num);
-      den = fmaf(w, ml[2 * s + 1], den);
-    }
-    o = nv > 0 ? num / den : 0.f;  // empty context: exact zeros
+    const int nv = (ctx + split_tokens - 1) / split_tokens;  // splits holding tokens
+    res = merge_row<D>(ws_acc, ws_ml, (size_t)row, num_splits, nv, d4);
   }
-  out[row * D + d] = f32_to_bf16(o);
+  store_bf16x4(out + (size_t)row * D + d4, res);
 }
 
 template <int D, int G>
 int launch_partition_dg(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
-  const dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  const dim3 grid(a.num_splits * a.num_kv_heads * a.batch);
   const size_t lds = sizeof(float) * lds_words<D, G>(a.split_pages);
   void* args[] = {(void*)&a.q,           (void*)&a.k_cache,      (void*)&a.v_cache,
                   (void*)&a.block_table, (void*)&a.context_lens, (void*)&a.ws_acc,
@@ -409,13 +476,15 @@ int launch_partition_dg(const LaunchArgs& a) {
 template <int D>
 int launch_reduce_d(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
+  const int rows = a.batch * a.num_q_heads;
   const int split_tokens = a.split_pages * kPage;
   const int max_ctx = a.max_pages * kPage;
-  void* args[] = {(void*)&a.ws_acc,     (void*)&a.ws_ml,       (void*)&a.context_lens,
-                  (void*)&a.out,        (void*)&a.num_q_heads, (void*)&a.num_splits,
-                  (void*)&split_tokens, (void*)&max_ctx};
+  constexpr int RPW = kThreads / (D / 4);
+  void* args[] = {(void*)&a.ws_acc,      (void*)&a.ws_ml,      (void*)&a.context_lens,
+                  (void*)&a.out,         (void*)&rows,         (void*)&a.num_q_heads,
+                  (void*)&a.num_splits,  (void*)&split_tokens, (void*)&max_ctx};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel<D>),
-                              dim3(a.num_q_heads, a.batch), dim3(D), args, 0, stream);
+                              dim3((rows + RPW - 1) / RPW), dim3(kThreads), args, 0, stream);
 }
 
 typedef int (*LaunchFn)(const LaunchArgs&);

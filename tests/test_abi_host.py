@@ -67,9 +67,9 @@ def test_struct_layout_matches_header():
 
 @pytest.mark.parametrize("cfg,expect", [
     ((2, 40, 8, 128, 2, 4), (1, 2)),       # B=2, W=2: one page per split
-    ((16, 40, 8, 128, 32, 512), (4, 8)),   # 128 (seq, kv head) pairs -> 8 splits of 512 tokens
-    ((256, 40, 8, 128, 32, 2050), (4, 8)),
-    ((32, 16, 2, 256, 32, 1024), (2, 16)), # 64 pairs -> 16 splits of 256 tokens
+    ((16, 40, 8, 128, 32, 512), (8, 4)),   # 128 (seq, kv head) pairs -> 4 splits of 1024 tokens
+    ((256, 40, 8, 128, 32, 2050), (8, 4)), # one split wanted; 32 KiB score tile caps it at 8 pages
+    ((32, 16, 2, 256, 32, 1024), (4, 8)),  # 64 pairs -> 8 splits of 512 tokens
 ])
 def test_plan_for_the_standard_workloads(cfg, expect):
     plan = pa.pa_plan(pa.make_shape(*cfg))

@@ -248,7 +248,7 @@ def test_merge_stage_on_oracle_partials():
                                                    V[s * T:(s + 1) * T, h], s64)
                 acc[b, hq, s] = a
                 ml[b, hq, s] = (m * math.log2(math.e), l)
-    ws = np.zeros(plan.workspace_bytes, np.uint8)
+    ws = np.zeros(plan.workspace_bytes, np.uint8)  # acc at 0, ml after it (256-aligned)
     off = (acc.nbytes + 255) // 256 * 256
     ws[:acc.nbytes] = acc.view(np.uint8).ravel()
     ws[off:off + ml.nbytes] = ml.view(np.uint8).ravel()
@@ -261,3 +261,74 @@ def test_merge_stage_on_oracle_partials():
     assert np.array_equal(got[3], np.zeros_like(got[3]))
     # exact partials: the only error left is FP32 merging and the BF16 rounding
     assert np.max(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)) <= 1e-6
+
+
+def test_decode_equals_two_stage_call():
+    # pa_decode and pa_decode_partials + pa_merge_partials run the same
+    # kernels: identical bits, in every plan
+    announce("pa_decode vs two-stage")
+    from paged_gqa_attention_amd import pagedattn as pa
+    for cfg, sp in ((2, 0), (2, 1), (5, 0), (4, 0)):
+        w = workloads.config(cfg)
+        t = to_device(w)
+        fused = run_gpu(w, tensors=t, split_pages=sp)
+        shape = pa.shape_of(w.q, w.k_cache, w.block_table, sp)
+        ws = torch.zeros(pa.pa_workspace_size(shape), dtype=torch.uint8, device="cuda:0")
+        pa.pa_decode_partials(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                              t["context_lens"], ws, scale=w.scale, split_pages=sp)
+        out = torch.empty_like(t["q"])
+        pa.pa_merge_partials(shape, t["context_lens"], ws, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), fused), (cfg, sp)
+
+
+def test_stale_workspace_and_many_calls():
+    # a workspace full of garbage and reused across shapes: its contents
+    # between calls do not matter
+    announce("stale workspace")
+    from paged_gqa_attention_amd import pagedattn as pa
+    ws = torch.full((64 << 20,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    outs = {}
+    for rep in range(3):
+        for cfg in (1, 2, 5):
+            w = workloads.config(cfg)
+            t = to_device(w)
+            o = pa.pa_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                             t["context_lens"], scale=w.scale, workspace=ws)
+            torch.cuda.synchronize()
+            o = o.cpu()
+            if rep == 0:
+                outs[cfg] = o
+                assert_parity(o, run_oracle(w), f"stale ws config{cfg}")
+            else:
+                assert torch.equal(o, outs[cfg])
+
+
+def test_graph_capture_replays():
+    # pa_decode allocates nothing and never synchronises: capture it in a graph,
+    # replay it several times with eager calls in between, compare every replay
+    announce("graph capture")
+    from paged_gqa_attention_amd import pagedattn as pa
+    w = workloads.config(2)
+    t = to_device(w)
+    shape = pa.shape_of(w.q, w.k_cache, w.block_table)
+    ws = torch.zeros(pa.pa_workspace_size(shape), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(t["q"])
+    eager = run_gpu(w, tensors=t)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        pa.pa_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+                     scale=w.scale, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.pa_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+                     scale=w.scale, out=out, workspace=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), eager), rep
+        assert torch.equal(run_gpu(w, tensors=t), eager)   # eager work between replays
