@@ -338,6 +338,31 @@ def main():
             print(f"[bench] config{cfg}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
             del sets, ds, wsx
             torch.cuda.empty_cache()
+        # paged KV write: a decode step's 16 rows (launch-bound) and a bulk write
+        # of 65,536 rows (a whole 16 x 4096 cache; HBM-bound, 4 row-moves/token)
+        Hkv, D = 8, 128
+        row_bytes = Hkv * D * 2
+        kc = torch.empty(512 * 128, Hkv, D, dtype=torch.bfloat16, device=dev).view(512, 128, Hkv, D)
+        vc = torch.empty_like(kc)
+        for T in (16, 65536):
+            gen = torch.Generator(device=dev).manual_seed(T)
+            kn = torch.randn(T, Hkv, D, device=dev, generator=gen).to(torch.bfloat16)
+            vn = torch.randn(T, Hkv, D, device=dev, generator=gen).to(torch.bfloat16)
+            slots = torch.randperm(512 * 128, device=dev, generator=gen)[:T].to(torch.int32)
+            wshape = pa.PaKvWriteShape(T, Hkv, D, 128, 512)
+            import ctypes
+            wargs = (ctypes.byref(wshape), kn.data_ptr(), vn.data_ptr(), slots.data_ptr(),
+                     kc.data_ptr(), vc.data_ptr(), stream)
+            ms = timed(torch, [lambda: pa.lib.pa_kv_write(*wargs)], 200, 10)
+            moved = 4 * T * row_bytes
+            extra[f"kv_write_T{T}"] = {
+                "description": f"paged KV write of {T} tokens, Hkv 8, D 128, random distinct slots",
+                "us_per_call": round(ms * 1e3, 2),
+                "bytes_moved_per_call": moved,
+                "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+            }
+            print(f"[bench] kv_write T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+        del kc, vc
         result["other_workloads"] = extra
 
     if args.calibrate_copy:

@@ -163,6 +163,34 @@ pa_status_t pa_merge_partials(const pa_shape_t* shape, const int32_t* context_le
                               const void* workspace, size_t workspace_bytes, void* out,
                               void* stream);
 
+/* ---- paged KV write ------------------------------------------------------
+ * Store a step's new K/V rows into the pools before attention reads them: the
+ * scatter of "Qwen 3" (TensorSharp docs), section 11, which writes each token's
+ * K and V at block_id * block_size + offset of the layer's paged buffer.
+ * Token t goes to page slot_mapping[t] / page_size, position
+ * slot_mapping[t] % page_size, for all KV heads at once. */
+typedef struct {
+  int32_t num_tokens;         /* T >= 0 (T == 0: nothing to do, PA_OK)          */
+  int32_t num_kv_heads;       /* Hkv >= 1                                       */
+  int32_t head_dim;           /* D: a multiple of 8 in [8, 1024]                */
+  int32_t page_size;          /* P == 128                                       */
+  int32_t num_pages;          /* N >= 1: pages in each pool                     */
+} pa_kv_write_shape_t;
+
+/* Enqueue the write on `stream`.
+ *   k_new, v_new  device, BF16 [T, Hkv, D], 16-byte aligned
+ *   slot_mapping  device, INT32 [T]: flat slot page * P + position; a negative
+ *                 slot marks a padding token and writes nothing; a slot at or
+ *                 past N * P is a caller error and also writes nothing (the
+ *                 kernel never writes outside the pools)
+ *   k_cache,      device, BF16 [N, P, Hkv, D], 16-byte aligned; updated in place
+ *   v_cache       (must not alias each other or the new rows)
+ * Two tokens with the same slot in one call: which one lands is unspecified.
+ * Returns PA_OK once the kernel is enqueued; no host reads of device data. */
+pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
+                        const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

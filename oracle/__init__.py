@@ -11,5 +11,6 @@ from .decode import (  # noqa: F401
     gather_sequence,
     lse_merge,
     paged_decode_attention,
+    paged_kv_write,
     partial_attention,
 )

@@ -27,8 +27,8 @@ So for every sequence b, query head hq and its KV head h:
 
 over t in [0, context_lens[b]), with K_b / V_b the sequence's gathered pages.
 
-Readings of points the pages leave open (each is listed in the design notes)
----------------------------------------------------------------------------
+Readings of points the pages leave open
+---------------------------------------
 R1  Query head hq uses KV head ``hq // G`` with G = Hq // Hkv (consecutive
     grouping), the layout the fused QKV row order [qDim | kvDim | kvDim] and
     the per-KV-head padding of query heads on the orcarouter page imply.
@@ -47,8 +47,11 @@ All arithmetic is FP64. Inputs are BF16 values (held in any float array; a BF16
 value widens exactly to FP64). The output is FP64; a GPU result rounded to BF16
 is compared against it.
 
-Parity pins (checked by tests/test_oracle_pins.py against things other than
-this file): a pure-Python scalar brute force, torch's CPU scaled-dot-product
+``paged_kv_write`` is the plain index write that stores a step's new K/V rows
+into the pools before attention reads them.
+
+Parity pins (checked by tests/test_oracle_pins.py and tests/test_oracle_kv_write.py
+against things other than this file): a pure-Python scalar brute force, torch's CPU scaled-dot-product
 attention in FP64, closed forms (context 1, uniform scores, a one-hot limit,
 hand-derived two-token values), paged == contiguous layouts, invariance under
 a permutation of the page pool, shared physical pages, the [K,V]/[q,0]
@@ -68,6 +71,7 @@ __all__ = [
     "gather_sequence",
     "partial_attention",
     "lse_merge",
+    "paged_kv_write",
 ]
 
 
@@ -235,3 +239,33 @@ def lse_merge(parts):
         num = num + w * acc
         den += w * l
     return num / den
+
+
+def paged_kv_write(k_cache, v_cache, k_new, v_new, slot_mapping):
+    """Scatter new K/V rows into the paged pools; returns new (k_cache, v_cache).
+
+    "Qwen 3" (TensorSharp docs), section 11 "Batched / paged forward": the
+    layer's K and V of every token are written at block_id * block_size +
+    offset of the paged buffer. Here ``slot_mapping[t]`` is that flat slot for
+    token t: page ``slot // P``, position ``slot % P``. A negative slot marks a
+    padding token that writes nothing (reading of the pages' -1 padding);
+    slots at or past ``num_pages * P`` are caller errors and are skipped too,
+    so nothing outside the pool is written.
+
+    k_cache, v_cache  [N, P, Hkv, D]      (any dtype; copied, not modified)
+    k_new, v_new      [T, Hkv, D]
+    slot_mapping      [T] int
+    """
+    k = np.array(k_cache, copy=True)
+    v = np.array(v_cache, copy=True)
+    N, P = k.shape[0], k.shape[1]
+    slots = _as_i64(slot_mapping)
+    kn = np.asarray(k_new)
+    vn = np.asarray(v_new)
+    for t, slot in enumerate(slots.tolist()):
+        if slot < 0 or slot >= N * P:
+            continue
+        page, pos = divmod(slot, P)
+        k[page, pos] = kn[t]
+        v[page, pos] = vn[t]
+    return k, v

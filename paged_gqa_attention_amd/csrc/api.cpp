@@ -221,4 +221,37 @@ pa_status_t pa_merge_partials(const pa_shape_t* shape, const int32_t* context_le
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
+                        const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                        void* stream) {
+  if (!shape) return PA_ERR_NULL_POINTER;
+  if (shape->num_tokens < 0 || shape->num_kv_heads < 1 || shape->head_dim < 1 ||
+      shape->page_size < 1 || shape->num_pages < 1)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (shape->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+  if (shape->head_dim % 8 != 0 || shape->head_dim > 1024 || shape->num_kv_heads > 4096)
+    return PA_ERR_UNSUPPORTED;
+  // the kernel's grid covers num_tokens * row chunks in one 1-D launch
+  const long long chunks = (long long)shape->num_tokens * shape->num_kv_heads * shape->head_dim / 8;
+  if (chunks > (long long)INT32_MAX * 256) return PA_ERR_UNSUPPORTED;
+  if (shape->num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL_POINTER;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)slot_mapping & 3u))
+    return PA_ERR_INVALID_ARGUMENT;
+  pa::KvWriteArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = shape->num_tokens;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.page_size = shape->page_size;
+  a.num_pages = shape->num_pages;
+  a.stream = stream;
+  return pa::launch_kv_write(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -35,4 +35,18 @@ size_t partition_lds_bytes(int head_dim, int gqa_ratio, int split_pages);
 int launch_partition(const LaunchArgs& a);
 int launch_reduce(const LaunchArgs& a);
 
+// Arguments of the paged KV write, already validated on the host.
+struct KvWriteArgs {
+  const void* k_new;          // bf16 [T, Hkv, D]
+  const void* v_new;          // bf16 [T, Hkv, D]
+  const int32_t* slot_mapping;// int32 [T]
+  void* k_cache;              // bf16 [N, P, Hkv, D]
+  void* v_cache;              // bf16 [N, P, Hkv, D]
+  int num_tokens, num_kv_heads, head_dim, page_size, num_pages;
+  void* stream;               // hipStream_t
+};
+
+// Enqueue the KV write kernel; 0 on success, else the HIP error code.
+int launch_kv_write(const KvWriteArgs& a);
+
 }  // namespace pa

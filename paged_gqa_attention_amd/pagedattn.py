@@ -52,6 +52,16 @@ class PaPlan(ctypes.Structure):
     ]
 
 
+class PaKvWriteShape(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+    ]
+
+
 class PagedAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -88,6 +98,11 @@ def _load():
     lib.pa_merge_partials.argtypes = [
         ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.pa_kv_write.restype = ctypes.c_int
+    lib.pa_kv_write.argtypes = [
+        ctypes.POINTER(PaKvWriteShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
     return lib
 
@@ -236,3 +251,32 @@ def pa_merge_partials(shape: PaShape, context_lens: torch.Tensor, workspace: tor
     if st != PA_OK:
         raise PagedAttnError(st, "pa_merge_partials")
     return out
+
+
+def pa_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write new K/V rows [T, Hkv, D] into the pools at flat slots (in place).
+
+    slot = page * 128 + position; negative slots are padding and write nothing.
+    """
+    if k_new.dim() != 3 or v_new.shape != k_new.shape or k_cache.dim() != 4 \
+            or v_cache.shape != k_cache.shape or k_cache.shape[2:] != k_new.shape[1:]:
+        raise ValueError("expected k_new/v_new [T, Hkv, D] and caches [N, P, Hkv, D]")
+    if slot_mapping.shape != (k_new.shape[0],):
+        raise ValueError("slot_mapping must be [T]")
+    for name, t, dt in (("k_new", k_new, torch.bfloat16), ("v_new", v_new, torch.bfloat16),
+                        ("k_cache", k_cache, torch.bfloat16), ("v_cache", v_cache, torch.bfloat16),
+                        ("slot_mapping", slot_mapping, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != k_new.device or t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU of k_new")
+    T, Hkv, D = k_new.shape
+    shape = PaKvWriteShape(int(T), int(Hkv), int(D), int(k_cache.shape[1]), int(k_cache.shape[0]))
+    st = _lib.pa_kv_write(ctypes.byref(shape), k_new.data_ptr(), v_new.data_ptr(),
+                          slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                          _stream(k_new.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_kv_write")

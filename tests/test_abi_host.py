@@ -33,8 +33,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert names == ["pa_abi_version", "pa_decode", "pa_decode_partials", "pa_merge_partials",
-                     "pa_plan", "pa_status_string", "pa_workspace_size"]
+    assert names == ["pa_abi_version", "pa_decode", "pa_decode_partials", "pa_kv_write",
+                     "pa_merge_partials", "pa_plan", "pa_status_string", "pa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -175,3 +175,32 @@ def test_misaligned_pointers_scale_and_workspace():
     a = list(ok)
     a[8] = ws - 1
     assert pa.lib.pa_decode(ctypes.byref(s), *a) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_kv_write_shape_struct():
+    assert ctypes.sizeof(pa.PaKvWriteShape) == 5 * 4
+
+
+@fake_pointers
+def test_kv_write_rejects_bad_arguments():
+    d = 1 << 20
+    def call(shape, *ptrs):
+        return pa.lib.pa_kv_write(ctypes.byref(shape) if shape is not None else None, *ptrs)
+    ok = [d, d, d, d, d, None]
+    good = lambda: pa.PaKvWriteShape(16, 8, 128, 128, 64)
+    assert call(None, *ok) == pa.PA_ERR_NULL_POINTER
+    for field, value, code in (("num_tokens", -1, 2), ("num_kv_heads", 0, 2), ("head_dim", 0, 2),
+                               ("page_size", 64, 3), ("num_pages", 0, 2), ("head_dim", 12, 3),
+                               ("head_dim", 2048, 3)):
+        s = good()
+        setattr(s, field, value)
+        assert call(s, *ok) == code, field
+    for i in range(5):
+        a = list(ok)
+        a[i] = None
+        assert call(good(), *a) == pa.PA_ERR_NULL_POINTER, i
+    for i, bad in ((0, d + 8), (1, d + 2), (2, d + 2), (3, d + 4), (4, d + 8)):
+        a = list(ok)
+        a[i] = bad
+        assert call(good(), *a) == pa.PA_ERR_INVALID_ARGUMENT, i
+    assert call(pa.PaKvWriteShape(0, 8, 128, 128, 64), None, None, None, None, None, None) == pa.PA_OK
