@@ -338,6 +338,44 @@ def main():
             print(f"[bench] config{cfg}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
             del sets, ds, wsx
             torch.cuda.empty_cache()
+        # the bandwidth-stress workload over FP8-E4M3 pools: 40 layers of codes
+        # (quantised on the device with one scale per tensor), half the bytes
+        w3 = workloads.config(3)
+        shp = pa.shape_of(w3.q, w3.k_cache, w3.block_table)
+        wsx = torch.empty(pa.pa_plan(shp).workspace_bytes, dtype=torch.uint8, device=dev)
+        btx, ctxx = w3.block_table.to(dev), w3.context_lens.to(dev)
+        gen8 = torch.Generator(device=dev).manual_seed(808)
+        import ctypes
+        f8args = []
+        f8keep = []
+        for li in range(L):
+            qx = torch.randn(w3.q.shape, device=dev, generator=gen8).to(torch.bfloat16)
+            ks = []
+            for _ in range(2):
+                x = torch.randn(w3.k_cache.shape, device=dev, generator=gen8)
+                sc = float(x.abs().max()) / 448.0
+                ks.append(((x / sc).to(torch.float8_e4m3fn).view(torch.uint8), sc))
+                del x
+            ox = torch.empty_like(qx)
+            f8keep.append((qx, ks, ox))
+            f8args.append((ctypes.byref(shp), qx.data_ptr(), ks[0][0].data_ptr(),
+                           ks[1][0].data_ptr(), ctypes.c_float(ks[0][1]), ctypes.c_float(ks[1][1]),
+                           btx.data_ptr(), ctxx.data_ptr(), ctypes.c_float(w3.scale),
+                           ox.data_ptr(), wsx.data_ptr(), wsx.numel(), stream))
+        ms = timed(torch, [lambda a=a: pa.lib.pa_decode_fp8(*a) for a in f8args], 400, 40)
+        by = w3.kv_bytes() // 2
+        extra["config3_fp8"] = {
+            "description": "bandwidth stress over FP8-E4M3 K/V pools (per-tensor scales), 40 layers",
+            "us_per_call": round(ms * 1e3, 2),
+            "kv_bytes_per_call": by,
+            "kv_gbs": round(by / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_us": round(int(w3.context_lens.sum()) / (ms * 1e3), 1),
+        }
+        print(f"[bench] config3 fp8: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+        del f8args, f8keep, wsx
+        torch.cuda.empty_cache()
+
         # paged KV write: a decode step's 16 rows (launch-bound) and a bulk write
         # of 65,536 rows (a whole 16 x 4096 cache; HBM-bound, 4 row-moves/token)
         Hkv, D = 8, 128

@@ -135,6 +135,19 @@ pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cach
                       const int32_t* context_lens, float scale, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode attention over FP8 pools: k_cache and v_cache hold FP8 E4M3 codes
+ * (the OCP format: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, 0x7F/0xFF NaN), one byte per value in the same
+ * [page, token, kv_head, dim] order, and the values they stand for are
+ * code * k_scale and code * v_scale (one FP32 scale per tensor; finite).
+ * Everything else (q, out, tables, workspace, errors) is as for pa_decode.
+ * The fp8_e4m3 KV cache is the KV dtype the orcarouter page measures for
+ * decode; it halves the bytes each token costs. */
+pa_status_t pa_decode_fp8(const pa_shape_t* shape, const void* q, const void* k_cache,
+                          const void* v_cache, float k_scale, float v_scale,
+                          const int32_t* block_table, const int32_t* context_lens, float scale,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The two stages of pa_decode, for callers that move or combine split partials
  * themselves (for instance a context-parallel decode that gives each GPU a
  * range of pages and merges the partials after exchanging them). Together

@@ -8,9 +8,11 @@ back to it.
 from .decode import (  # noqa: F401
     attend,
     contiguous_decode_attention,
+    decode_fp8_e4m3,
     gather_sequence,
     lse_merge,
     paged_decode_attention,
+    paged_decode_attention_fp8,
     paged_kv_write,
     partial_attention,
 )

@@ -48,10 +48,12 @@ value widens exactly to FP64). The output is FP64; a GPU result rounded to BF16
 is compared against it.
 
 ``paged_kv_write`` is the plain index write that stores a step's new K/V rows
-into the pools before attention reads them.
+into the pools before attention reads them. ``paged_decode_attention_fp8``
+dequantises FP8-E4M3 pools (``decode_fp8_e4m3`` times a per-tensor scale) and
+then computes the same attention.
 
-Parity pins (checked by tests/test_oracle_pins.py and tests/test_oracle_kv_write.py
-against things other than this file): a pure-Python scalar brute force, torch's CPU scaled-dot-product
+Parity pins (checked by tests/test_oracle_pins.py, tests/test_oracle_kv_write.py
+and tests/test_oracle_fp8.py against things other than this file): a pure-Python scalar brute force, torch's CPU scaled-dot-product
 attention in FP64, closed forms (context 1, uniform scores, a one-hot limit,
 hand-derived two-token values), paged == contiguous layouts, invariance under
 a permutation of the page pool, shared physical pages, the [K,V]/[q,0]
@@ -72,6 +74,8 @@ __all__ = [
     "partial_attention",
     "lse_merge",
     "paged_kv_write",
+    "decode_fp8_e4m3",
+    "paged_decode_attention_fp8",
 ]
 
 
@@ -269,3 +273,36 @@ def paged_kv_write(k_cache, v_cache, k_new, v_new, slot_mapping):
         k[page, pos] = kn[t]
         v[page, pos] = vn[t]
     return k, v
+
+
+def decode_fp8_e4m3(codes) -> np.ndarray:
+    """FP8 E4M3 (the OCP "FN" variant) bytes to FP64 values.
+
+    Definition: sign bit s, 4 exponent bits e (bias 7), 3 mantissa bits m.
+    e = 0 is subnormal: (-1)^s * m * 2^-9; otherwise (-1)^s * (1 + m/8) *
+    2^(e-7); the two codes with e = 15, m = 7 are NaN; there is no infinity.
+    The KV-cache dtype choice is the one the orcarouter page measures
+    (fp8_e4m3 KV against NVFP4 KV in decode) and "Qwen 3" section 10 lists KV
+    dtype options for.
+    """
+    b = np.asarray(codes).astype(np.int64) & 0xFF
+    s = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = s * val
+    return np.where((e == 15) & ((b & 7) == 7), np.nan, val)
+
+
+def paged_decode_attention_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table,
+                               context_lens, scale):
+    """Decode attention over FP8-E4M3 K/V pools with per-tensor FP32 scales.
+
+    K = decode(k_codes) * k_scale and V = decode(v_codes) * v_scale (each
+    scale handed over as FP32, used exactly in FP64), then the same attention
+    as ``paged_decode_attention``. Reading: the pages do not fix the scale
+    granularity; one scale per tensor is the plainest one.
+    """
+    k = decode_fp8_e4m3(k_codes) * float(np.float32(k_scale))
+    v = decode_fp8_e4m3(v_codes) * float(np.float32(v_scale))
+    return paged_decode_attention(q, k, v, block_table, context_lens, scale)

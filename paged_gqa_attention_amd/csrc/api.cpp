@@ -154,8 +154,8 @@ pa_status_t prepare(const pa_shape_t* shape, const void* q, const void* k_cache,
 
   const size_t rows = (size_t)shape->batch * shape->num_q_heads * plan.num_splits;
   a->q = static_cast<const uint16_t*>(q);
-  a->k_cache = static_cast<const uint16_t*>(k_cache);
-  a->v_cache = static_cast<const uint16_t*>(v_cache);
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
   a->block_table = block_table;
   a->context_lens = context_lens;
   a->out = static_cast<uint16_t*>(out);
@@ -171,6 +171,8 @@ pa_status_t prepare(const pa_shape_t* shape, const void* q, const void* k_cache,
   a->split_pages = plan.split_pages;
   a->num_splits = plan.num_splits;
   a->score_scale = scale * 1.4426950408889634f;  // natural-exp softmax computed as exp2
+  a->v_scale = 1.0f;
+  a->kv_fp8 = false;
   a->stream = stream;
   return PA_OK;
 }
@@ -190,6 +192,26 @@ pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cach
   st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, out, workspace,
                workspace_bytes, stream, true, true, &a);
   if (st != PA_OK) return st;
+  if (pa::launch_partition(a) != 0) return PA_ERR_LAUNCH;
+  return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status_t pa_decode_fp8(const pa_shape_t* shape, const void* q, const void* k_cache,
+                          const void* v_cache, float k_scale, float v_scale,
+                          const int32_t* block_table, const int32_t* context_lens, float scale,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0) return PA_OK;
+  if (!isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_INVALID_ARGUMENT;
+  pa::LaunchArgs a;
+  st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, out, workspace,
+               workspace_bytes, stream, true, true, &a);
+  if (st != PA_OK) return st;
+  // K = code * k_scale enters the logits linearly: fold it into the score scale
+  a.score_scale = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
+  a.kv_fp8 = true;
   if (pa::launch_partition(a) != 0) return PA_ERR_LAUNCH;
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }

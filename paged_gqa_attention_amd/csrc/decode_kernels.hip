@@ -35,6 +35,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace pa {
@@ -49,6 +51,8 @@ constexpr int kVSlots = 2;      // register slots of the V pipeline
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -67,6 +71,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// FP8 E4M3 (OCP) -> FP32 for the 4 codes of a word, with gfx950's
+// v_cvt_pk_f32_fp8 (exact: every E4M3 value is an FP32 value).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+}
+
+// 8 FP8 codes (2 words) -> 8 BF16 values packed for an MFMA operand. Exact:
+// E4M3 values have 3 mantissa bits and exponents within BF16's range, so the
+// FP32 value's upper half is the BF16 value.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  float f[8];
+  fp8x4_to_f32(w0, f);
+  fp8x4_to_f32(w1, f + 4);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+  return r;
+}
 
 // Software pipeline over n items held in NB register slots (item i in slot
 // i % NB): items i+1 .. i+NB-1 are loading while item i is used. In the steady
@@ -180,18 +209,23 @@ __host__ __device__ constexpr int lds_words(int split_pages) {
   return lds_tile_words<D, G>(split_pages) + kRedWords + split_pages;
 }
 
-template <int D, int G>
+// kFp8: the K/V pools hold FP8 E4M3 codes (one byte per value) with
+// per-tensor scales; k_scale is folded into score_scale on the host and
+// v_scale multiplies the split's output sums. Otherwise they hold BF16.
+template <int D, int G, bool kFp8>
 __global__ __launch_bounds__(kThreads) void partition_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int num_kv_heads, int max_pages, int num_pages,
-    int split_pages, int num_splits, float score_scale) {
+    int split_pages, int num_splits, float score_scale, float v_scale) {
   static_assert(D == 128 || D == 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "gqa ratio");
+  constexpr int ESZ = kFp8 ? 1 : 2;       // bytes per cached K/V value
   constexpr int GP = HeadPad<G>::value;   // LDS row stride (floats)
   constexpr int GQ = (G + 3) / 4;         // MFMA lane groups holding real heads
   constexpr int KK = D / 32;              // MFMA k-steps per 16-token tile
+  constexpr int KL = KK * ESZ / 2;        // 16-byte K loads per lane per tile
   constexpr int LPR = D / 8;              // lanes per token row in P.V
   constexpr int RPI = 64 / LPR;           // token rows per load instruction in P.V
   constexpr int PV_U = 4;                 // load instructions per P.V block
@@ -230,14 +264,18 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   int page_id = -1;
   if ((int)threadIdx.x < split_pages && first_page + (int)threadIdx.x < max_pages)
     page_id = block_table[(size_t)b * max_pages + first_page + threadIdx.x];
-  // A operand of the score MFMA: lane (lq, lr) holds q[head lr][32*kk + 8*lq .. +7]
-  // (zero rows for heads >= G).
+  // A operand of the score MFMA: lane (lq, lr) holds 8 dims of q[head lr] per
+  // k-step (zero rows for heads >= G), the same dims its K operand holds:
+  // BF16 pools: k-step kk <-> dims 32*kk + 8*lq .. +7;
+  // FP8 pools:  k-step kk <-> dims 64*(kk/2) + 16*lq + 8*(kk%2) .. +7.
   u32x4 qa[KK];
   {
-    const uint16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)h * G + lr) * D + 8 * lq;
+    const uint16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)h * G + lr) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qa[kk] = (lr < G) ? load16(qrow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = kFp8 ? 64 * (kk >> 1) + 16 * lq + 8 * (kk & 1) : 32 * kk + 8 * lq;
+      qa[kk] = (lr < G) ? load16(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   int ctx = context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
@@ -251,37 +289,46 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     s_page[threadIdx.x] = (unsigned)page_id < (unsigned)num_pages ? page_id : -1;
   __syncthreads();
 
-  const size_t page_bytes = (size_t)kPage * num_kv_heads * D * sizeof(uint16_t);
-  const uint32_t row_bytes = (uint32_t)num_kv_heads * D * sizeof(uint16_t);  // token stride
-  const uint32_t head_bytes = (uint32_t)h * D * sizeof(uint16_t);
+  const size_t page_bytes = (size_t)kPage * num_kv_heads * D * ESZ;
+  const uint32_t row_bytes = (uint32_t)num_kv_heads * D * ESZ;  // token stride
+  const uint32_t head_bytes = (uint32_t)h * D * ESZ;
 
   // Base of the page holding local token tl (wave-uniform); bad -> pool start.
-  auto page_base = [&](const uint16_t* pool, int tl, bool& bad) -> const char* {
+  auto page_base = [&](const void* pool, int tl, bool& bad) -> const char* {
     const int page = __builtin_amdgcn_readfirstlane(s_page[tl >> 7]);
     bad = page < 0;
     return reinterpret_cast<const char*>(pool) + (size_t)(bad ? 0 : page) * page_bytes;
   };
 
   // ---- phase 1: scores = q . K^T on MFMA --------------------------------
-  // B operand: lane (lq, lr) holds K[token tl + lr][32*kk + 8*lq .. +7]; one
-  // load instruction covers 16 token rows x 64 contiguous bytes.
+  // B operand: lane (lq, lr) holds 8 dims of K[token tl + lr] per k-step (the
+  // dims of its A operand); load j brings bytes 64*j + 16*lq .. +15 of the
+  // row, so one load instruction covers 16 token rows x 64 contiguous bytes.
+  // FP8 codes are widened to BF16 exactly before the MFMA.
   const uint32_t k_lane_off = (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
-  auto load_k = [&](int tile, u32x4 (&buf)[KK], bool& bad) {
+  auto load_k = [&](int tile, u32x4 (&buf)[KL], bool& bad) {
     const int tl = tile * 16;
     const char* base = page_base(k_cache, tl, bad);
     const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + k_lane_off;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      buf[kk] = *reinterpret_cast<const u32x4*>(base + off + 64u * kk);
+    for (int j = 0; j < KL; ++j)
+      buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
   };
-  auto score_tile = [&](int tile, const u32x4 (&buf)[KK], bool bad) {
+  auto score_tile = [&](int tile, const u32x4 (&buf)[KL], bool bad) {
     const int tl = tile * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 kb;
+      if constexpr (kFp8) {
+        const u32x4 w = buf[kk >> 1];
+        kb = (kk & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+      } else {
+        kb = buf[kk];
+      }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
-                                                    __builtin_bit_cast(bf16x8, buf[kk]), acc, 0,
-                                                    0, 0);
+                                                    __builtin_bit_cast(bf16x8, kb), acc, 0, 0, 0);
+    }
     // lane (lq, lr) holds S[head 4*lq + i][token tl + lr], i = 0..3
     if (lq < GQ) {
       const bool valid = tl + lr < n_s;
@@ -296,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const int ntile = (n_s + 15) >> 4;
   const int nk = ntile > wave ? (ntile - 1 - wave) / kWaves + 1 : 0;  // tiles of this wave
   {
-    u32x4 kbuf[KNB][KK];
+    u32x4 kbuf[KNB][KL];
     bool kbad[KNB];
     pipeline<KNB>(
         nk, [&](int i, int slot) { load_k(wave + i * kWaves, kbuf[slot], kbad[slot]); },
@@ -306,19 +353,21 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // ---- V loads of the first P.V step go out before the softmax ------------
   const int r = lane / LPR;  // token row inside a load instruction
   const int c = lane % LPR;  // 16-byte chunk of the row: dims 8c .. 8c+7
-  const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 16u * c;
-  auto load_v = [&](int blk, u32x4 (&buf)[PV_U]) {
+  // one lane loads the 8 values of dims 8c .. 8c+7 (16 B of BF16, 8 B of FP8)
+  using VChunk = typename std::conditional<kFp8, u32x2, u32x4>::type;
+  const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 8u * ESZ * c;
+  auto load_v = [&](int blk, VChunk (&buf)[PV_U]) {
     const int tl = blk * BR;
     bool bad;
     const char* base = page_base(v_cache, tl, bad);  // bad pages: scores are NaN already
     const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + v_lane_off;
 #pragma unroll
     for (int u = 0; u < PV_U; ++u)
-      buf[u] = *reinterpret_cast<const u32x4*>(base + off + (uint32_t)(u * RPI) * row_bytes);
+      buf[u] = *reinterpret_cast<const VChunk*>(base + off + (uint32_t)(u * RPI) * row_bytes);
   };
   const int nblk = (n_s + BR - 1) / BR;
   const int nv = nblk > wave ? (nblk - 1 - wave) / kWaves + 1 : 0;  // blocks of this wave
-  u32x4 vbuf[VNB][PV_U];
+  VChunk vbuf[VNB][PV_U];
 #pragma unroll
   for (int i = 0; i < VNB - 1; ++i)
     if (i < nv) load_v(wave + i * kWaves, vbuf[i]);
@@ -360,21 +409,26 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
 
-  auto pv_block = [&](int blk, u32x4 (&buf)[PV_U]) {
+  auto pv_block = [&](int blk, VChunk (&buf)[PV_U]) {
     const int tl = blk * BR;
     if (tl + BR > n_s) {  // last block: rows past the context may hold NaN
 #pragma unroll
       for (int u = 0; u < PV_U; ++u)
-        if (tl + u * RPI + r >= n_s) buf[u] = u32x4{0u, 0u, 0u, 0u};
+        if (tl + u * RPI + r >= n_s) buf[u] = VChunk{};
     }
 #pragma unroll
     for (int u = 0; u < PV_U; ++u) {
       const int t = tl + u * RPI + r;
       float v[8];
+      if constexpr (kFp8) {
+        fp8x4_to_f32(buf[u][0], v);
+        fp8x4_to_f32(buf[u][1], v + 4);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_lo(buf[u][i]);
-        v[2 * i + 1] = bf16_hi(buf[u][i]);
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_lo(buf[u][i]);
+          v[2 * i + 1] = bf16_hi(buf[u][i]);
+        }
       }
       float p[G];
 #pragma unroll
@@ -431,7 +485,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int g = i / D;
     const int d = i - g * D;
-    dst[(size_t)g * num_splits * D + d] = ra[i] + ra[G * D + i];
+    const float sum = ra[i] + ra[G * D + i];
+    dst[(size_t)g * num_splits * D + d] = kFp8 ? sum * v_scale : sum;
   }
 }
 
@@ -459,8 +514,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
   store_bf16x4(out + (size_t)row * D + d4, res);
 }
 
-template <int D, int G>
-int launch_partition_dg(const LaunchArgs& a) {
+template <int D, int G, bool kFp8>
+int launch_partition_dgt(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const dim3 grid(a.num_splits * a.num_kv_heads * a.batch);
   const size_t lds = sizeof(float) * lds_words<D, G>(a.split_pages);
@@ -468,9 +523,14 @@ int launch_partition_dg(const LaunchArgs& a) {
                   (void*)&a.block_table, (void*)&a.context_lens, (void*)&a.ws_acc,
                   (void*)&a.ws_ml,       (void*)&a.num_kv_heads, (void*)&a.max_pages,
                   (void*)&a.num_pages,   (void*)&a.split_pages,  (void*)&a.num_splits,
-                  (void*)&a.score_scale};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G>), grid,
-                              dim3(kThreads), args, lds, stream);
+                  (void*)&a.score_scale, (void*)&a.v_scale};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G, kFp8>),
+                              grid, dim3(kThreads), args, lds, stream);
+}
+
+template <int D, int G>
+int launch_partition_dg(const LaunchArgs& a) {
+  return a.kv_fp8 ? launch_partition_dgt<D, G, true>(a) : launch_partition_dgt<D, G, false>(a);
 }
 
 template <int D>

@@ -10,8 +10,8 @@ namespace pa {
 // Everything the two kernels need for one call, already validated on the host.
 struct LaunchArgs {
   const uint16_t* q;          // bf16 [B, Hq, D]
-  const uint16_t* k_cache;    // bf16 [N, P, Hkv, D]
-  const uint16_t* v_cache;    // bf16 [N, P, Hkv, D]
+  const void* k_cache;        // bf16 or fp8-e4m3 [N, P, Hkv, D]
+  const void* v_cache;        // bf16 or fp8-e4m3 [N, P, Hkv, D]
   const int32_t* block_table; // int32 [B, W]
   const int32_t* context_lens;// int32 [B]
   uint16_t* out;              // bf16 [B, Hq, D]
@@ -19,7 +19,9 @@ struct LaunchArgs {
   float* ws_ml;               // f32 [B, Hq, S, 2]   (max, sum) per split, log2 units
   int batch, num_q_heads, num_kv_heads, head_dim, max_pages, num_pages;
   int split_pages, num_splits;
-  float score_scale;          // scale * log2(e), applied to q.k in FP32
+  float score_scale;          // scale * log2(e) (* k_scale for FP8), applied to q.k in FP32
+  float v_scale;              // FP8 pools: multiplies the split's output sums
+  bool kv_fp8;                // the pools hold FP8 E4M3 codes
   void* stream;               // hipStream_t
 };
 

@@ -99,6 +99,12 @@ def _load():
         ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.pa_decode_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8.argtypes = [
+        ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
     lib.pa_kv_write.restype = ctypes.c_int
     lib.pa_kv_write.argtypes = [
         ctypes.POINTER(PaKvWriteShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -219,6 +225,48 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                         workspace.numel() * workspace.element_size(), _stream(q.device))
     if st != PA_OK:
         raise PagedAttnError(st, "pa_decode")
+    return out
+
+
+def pa_decode_fp8(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                  k_scale: float, v_scale: float, block_table: torch.Tensor,
+                  context_lens: torch.Tensor, scale: Optional[float] = None,
+                  out: Optional[torch.Tensor] = None, split_pages: int = 0,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention over FP8-E4M3 pools (uint8 codes [N, 128, Hkv, D]) with
+    per-tensor scales: values are code * k_scale and code * v_scale."""
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise TypeError("k_codes and v_codes must be uint8 FP8-E4M3 codes")
+    B, Hq, D = q.shape
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.device.type != "cuda":
+        raise TypeError("q must be contiguous bf16 on the GPU")
+    if k_codes.dim() != 4 or v_codes.shape != k_codes.shape or k_codes.shape[3] != D:
+        raise ValueError("expected k_codes == v_codes shape [N, P, Hkv, D]")
+    for name, t, dt in (("k_codes", k_codes, torch.uint8), ("v_codes", v_codes, torch.uint8),
+                        ("block_table", block_table, torch.int32),
+                        ("context_lens", context_lens, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous {dt} on the GPU of q")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("expected block_table [B, W] and context_lens [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    shape = shape_of(q, k_codes, block_table, split_pages)
+    if B == 0:
+        return out
+    need = pa_workspace_size(shape)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    st = _lib.pa_decode_fp8(ctypes.byref(shape), q.data_ptr(), k_codes.data_ptr(),
+                            v_codes.data_ptr(), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                            block_table.data_ptr(), context_lens.data_ptr(), ctypes.c_float(scale),
+                            out.data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_decode_fp8")
     return out
 
 

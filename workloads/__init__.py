@@ -23,6 +23,9 @@ Recipe (shared by every workload)
 * ``scale`` defaults to the FP32 value of 1/sqrt(D) ("Qwen 3", TensorSharp
   docs, section 3: Q is multiplied by 1/sqrt(headDim)).
 
+``quantize_fp8`` prepares FP8-E4M3 pools (codes plus one FP32 scale per
+tensor) from a workload's BF16 pools; both sides then read the same codes.
+
 The five standard workloads follow the decode shapes of the pages: Qwen3-14B's
 40 query heads over 8 KV heads at head_dim 128, contexts up to 4096, and the
 (16, 2) head_dim-256 local head shape the orcarouter page lists.
@@ -222,3 +225,35 @@ def fill_unused_table(w: Workload, value: int = -1) -> Workload:
         n = int(w.context_lens[b])
         bt[b, -(-n // P):] = value
     return Workload(w.name + f"+table{value}", w.q, w.k_cache, w.v_cache, bt, w.context_lens, w.scale, dict(w.meta))
+
+
+FP8_E4M3_MAX = 448.0
+
+
+@dataclass
+class Fp8Pools:
+    """FP8-E4M3 K/V pools (raw bytes) with per-tensor FP32 scales."""
+    k_codes: torch.Tensor   # uint8 [N, P, Hkv, D]
+    v_codes: torch.Tensor   # uint8 [N, P, Hkv, D]
+    k_scale: float
+    v_scale: float
+
+
+def quantize_fp8(w: Workload) -> Fp8Pools:
+    """Per-tensor FP8-E4M3 quantisation of a workload's K and V pools.
+
+    scale = max|x| / 448 in FP32 (448 is the largest E4M3 value); codes are
+    x / scale rounded to the nearest E4M3 value by torch's conversion, after
+    clamping to +-448. NaN slots (poison) stay NaN codes.
+    """
+    def one(x):
+        xf = x.float()
+        finite = xf[torch.isfinite(xf)]
+        amax = float(finite.abs().max()) if finite.numel() else 1.0
+        scale = float(torch.tensor(max(amax, 1e-30) / FP8_E4M3_MAX, dtype=torch.float32))
+        y = torch.clamp(xf / scale, -FP8_E4M3_MAX, FP8_E4M3_MAX)
+        y = torch.where(torch.isnan(xf), xf, y)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+    kc, ks = one(w.k_cache)
+    vc, vs = one(w.v_cache)
+    return Fp8Pools(kc, vc, ks, vs)
