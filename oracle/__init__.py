@@ -14,5 +14,6 @@ from .decode import (  # noqa: F401
     paged_decode_attention,
     paged_decode_attention_fp8,
     paged_kv_write,
+    paged_multi_query_attention,
     partial_attention,
 )

@@ -50,10 +50,12 @@ is compared against it.
 ``paged_kv_write`` is the plain index write that stores a step's new K/V rows
 into the pools before attention reads them. ``paged_decode_attention_fp8``
 dequantises FP8-E4M3 pools (``decode_fp8_e4m3`` times a per-tensor scale) and
-then computes the same attention.
+then computes the same attention. ``paged_multi_query_attention`` handles
+several causal query tokens per sequence (chunked prefill, multi-token decode).
 
-Parity pins (checked by tests/test_oracle_pins.py, tests/test_oracle_kv_write.py
-and tests/test_oracle_fp8.py against things other than this file): a pure-Python scalar brute force, torch's CPU scaled-dot-product
+Parity pins (checked by tests/test_oracle_pins.py, tests/test_oracle_kv_write.py,
+tests/test_oracle_fp8.py and tests/test_oracle_multi_query.py against things
+other than this file): a pure-Python scalar brute force, torch's CPU scaled-dot-product
 attention in FP64, closed forms (context 1, uniform scores, a one-hot limit,
 hand-derived two-token values), paged == contiguous layouts, invariance under
 a permutation of the page pool, shared physical pages, the [K,V]/[q,0]
@@ -76,6 +78,7 @@ __all__ = [
     "paged_kv_write",
     "decode_fp8_e4m3",
     "paged_decode_attention_fp8",
+    "paged_multi_query_attention",
 ]
 
 
@@ -306,3 +309,48 @@ def paged_decode_attention_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tabl
     k = decode_fp8_e4m3(k_codes) * float(np.float32(k_scale))
     v = decode_fp8_e4m3(v_codes) * float(np.float32(v_scale))
     return paged_decode_attention(q, k, v, block_table, context_lens, scale)
+
+
+def paged_multi_query_attention(q, k_cache, v_cache, block_table, context_lens, query_start,
+                                scale):
+    """Several query tokens per sequence (chunked prefill, multi-token decode).
+
+    q [T, Hq, D] holds the query tokens of all sequences packed token-major,
+    sequence b owning rows query_start[b] .. query_start[b+1]-1 ("Qwen3-14B"
+    pypto-lib page, prefill_fwd: inputs packed token-major, T = sum of chunk
+    lengths, no batch padding). The Lq_b query tokens are the last Lq_b
+    tokens of sequence b's context_lens[b] cached tokens (their K/V were
+    written first, as in decode), so query i (position ctx - Lq + i) attends
+    causally to tokens [0, ctx - Lq + i] ("Qwen 3" TensorSharp docs, section
+    4.1: standard causal attention). A query that sees no token (ctx < Lq)
+    is a fully masked row and gives zeros, the convention the orcarouter
+    Qwen4-Exp QSA prefill page keeps for such rows ("operational details"
+    list, size-limits item). Returns out [T, Hq, D] FP64.
+    """
+    q = _as_f64(q)
+    k_cache = _as_f64(k_cache)
+    v_cache = _as_f64(v_cache)
+    block_table = _as_i64(block_table)
+    context_lens = _as_i64(context_lens)
+    qs = _as_i64(query_start)
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    G = Hq // Hkv
+    s64 = float(np.float32(scale))
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for b in range(len(context_lens)):
+        lq = int(qs[b + 1] - qs[b])
+        ctx = int(context_lens[b])
+        if lq == 0 or ctx <= 0:
+            continue
+        K = gather_sequence(k_cache, block_table[b], ctx)
+        V = gather_sequence(v_cache, block_table[b], ctx)
+        for i in range(lq):
+            n = ctx - lq + i + 1                 # tokens query i may see
+            if n <= 0:
+                continue
+            r = int(qs[b]) + i
+            for hq in range(Hq):
+                h = hq // G
+                out[r, hq] = attend(q[r, hq], K[:n, h, :], V[:n, h, :], s64)
+    return out

@@ -1,0 +1,79 @@
+"""Pins for the oracle's multi-query (chunked-prefill) attention."""
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+
+def _packed(seed, lqs, ctxs, Hq=10, Hkv=2, D=16):
+    gen = torch.Generator().manual_seed(seed)
+    w = workloads.build(len(ctxs), Hq, Hkv, D, ctxs, seed=seed, gen=gen,
+                        max_pages=max(-(-c // 128) for c in ctxs), pool="packed")
+    T = sum(lqs)
+    q = torch.randn(T, Hq, D, generator=gen).to(torch.bfloat16)
+    qs = torch.tensor([0] + list(np.cumsum(lqs)), dtype=torch.int32)
+    return w, q, qs
+
+
+def test_single_query_is_decode():
+    w, q, qs = _packed(1, [1, 1, 1], [5, 130, 300])
+    a = oracle.paged_multi_query_attention(q, w.k_cache, w.v_cache, w.block_table,
+                                           w.context_lens, qs, w.scale)
+    b = oracle.paged_decode_attention(q, w.k_cache, w.v_cache, w.block_table,
+                                      w.context_lens, w.scale)
+    assert np.array_equal(a, b)
+
+
+def test_matches_torch_causal_sdpa():
+    # each sequence's chunk against torch SDPA (FP64, CPU) with an explicit
+    # causal mask offset by the cached prefix
+    lqs, ctxs = [4, 1, 7], [9, 128, 200]
+    w, q, qs = _packed(2, lqs, ctxs)
+    got = oracle.paged_multi_query_attention(q, w.k_cache, w.v_cache, w.block_table,
+                                             w.context_lens, qs, w.scale)
+    Hq, Hkv, D = 10, 2, 16
+    for b, (lq, ctx) in enumerate(zip(lqs, ctxs)):
+        npg = -(-ctx // 128)
+        idx = w.block_table[b, :npg].long()
+        K = w.k_cache.index_select(0, idx).double().reshape(-1, Hkv, D)[:ctx]
+        V = w.v_cache.index_select(0, idx).double().reshape(-1, Hkv, D)[:ctx]
+        K = K.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        V = V.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        qb = q[int(qs[b]):int(qs[b + 1])].double().permute(1, 0, 2)      # [Hq, lq, D]
+        pos = torch.arange(ctx - lq, ctx).unsqueeze(1)
+        mask = torch.arange(ctx).unsqueeze(0) <= pos                     # [lq, ctx]
+        ref = F.scaled_dot_product_attention(qb, K, V, attn_mask=mask,
+                                             scale=float(np.float32(w.scale)))
+        assert np.max(np.abs(got[int(qs[b]):int(qs[b + 1])] - ref.permute(1, 0, 2).numpy())) <= 1e-12
+
+
+def test_later_tokens_do_not_leak():
+    # query i must not depend on cached tokens after its own position
+    lqs, ctxs = [5], [260]
+    w, q, qs = _packed(3, lqs, ctxs)
+    a = oracle.paged_multi_query_attention(q, w.k_cache, w.v_cache, w.block_table,
+                                           w.context_lens, qs, w.scale)
+    k = w.k_cache.clone()
+    v = w.v_cache.clone()
+    page = int(w.block_table[0, 2])          # tokens 256..259: positions of queries 1..4
+    k[page, 3] = 100.0                       # token 259 (the last query's own position)
+    v[page, 3] = -50.0
+    b = oracle.paged_multi_query_attention(q, k, v, w.block_table, w.context_lens, qs, w.scale)
+    assert np.array_equal(a[:4], b[:4])      # queries at 255..258 never see token 259
+    assert not np.array_equal(a[4], b[4])
+
+
+def test_empty_chunks_and_short_context():
+    w, q, qs = _packed(4, [0, 3, 0], [10, 2, 5])
+    out = oracle.paged_multi_query_attention(q, w.k_cache, w.v_cache, w.block_table,
+                                             w.context_lens, qs, w.scale)
+    # sequence 1 has ctx 2 < lq 3: its first query sees nothing -> zeros
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert np.all(np.isfinite(out))
+    # its last query sees both tokens: a two-token softmax
+    assert not np.array_equal(out[2], np.zeros_like(out[2]))
