@@ -204,6 +204,63 @@ pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, con
                         const int32_t* slot_mapping, void* k_cache, void* v_cache,
                         void* stream);
 
+/* ---- multi-query attention (chunked prefill, multi-token decode) ----------
+ * Several query tokens per sequence over the same paged cache. The query
+ * tokens of all sequences are packed token-major ("Qwen3-14B" pypto-lib page,
+ * prefill_fwd section: T = sum of the chunk lengths, no padding): sequence b
+ * owns rows query_start[b] .. query_start[b+1]-1 of q and out. They are the
+ * last Lq_b = query_start[b+1] - query_start[b] of its context_lens[b] cached
+ * tokens (their K/V already written, e.g. by pa_kv_write), so with causal
+ * masking ("Qwen 3" TensorSharp docs, section 4.1: standard causal attention)
+ * query i of sequence b attends to tokens [0, context_lens[b] - Lq_b + i]:
+ *
+ *   out[t, hq, :] = softmax_u( scale * q[t, hq, :] . K_b[u, h, :] ) @ V_b[u, h, :]
+ *
+ * with t = query_start[b] + i, h = hq / G and u over those tokens. A row that
+ * sees no token (context_lens[b] < Lq_b) is exactly zero. Lq_b == 1 is decode. */
+typedef struct {
+  int32_t batch;              /* B >= 0 sequences (B == 0: nothing to do)        */
+  int32_t num_tokens;         /* T >= 0 query rows of q and out (T == 0: PA_OK)  */
+  int32_t max_query_len;      /* >= 1: bound on every Lq_b; sizes the launch     */
+  int32_t num_q_heads;        /* Hq >= 1, multiple of num_kv_heads               */
+  int32_t num_kv_heads;       /* Hkv >= 1                                        */
+  int32_t head_dim;           /* D in {128, 256}                                 */
+  int32_t page_size;          /* P == 128                                        */
+  int32_t max_pages_per_seq;  /* W >= 1: row length (stride) of block_table      */
+  int32_t num_pages;          /* N >= 1: pages in each of k_cache and v_cache    */
+  int32_t split_pages;        /* pages per split; 0 lets the library choose      */
+} pa_mq_shape_t;
+
+/* Fill `plan` for a multi-query shape (host arithmetic only). One split needs
+ * no workspace (workspace_bytes == 0); more splits keep FP32 partials
+ * acc [T][Hq][S][D] and ml [T][Hq][S][2] laid out as for pa_decode_partials. */
+pa_status_t pa_mq_plan(const pa_mq_shape_t* shape, pa_plan_t* plan);
+
+/* Enqueue multi-query attention on `stream`.
+ *   q            device, BF16 [T, Hq, D], 16-byte aligned
+ *   k_cache,     device, BF16 [N, P, Hkv, D], 16-byte aligned
+ *   v_cache
+ *   block_table  device, INT32 [B, W] (as for pa_decode)
+ *   context_lens device, INT32 [B], in [0, W * P]; outside: the sequence's rows
+ *                are NaN
+ *   query_start  device, INT32 [B + 1], non-decreasing, query_start[0] >= 0,
+ *                query_start[B] <= T; a sequence whose range leaves [0, T] or
+ *                is longer than max_query_len is skipped (its rows are not
+ *                written); rows no sequence owns are not written
+ *   scale        finite FP32 logit scale
+ *   out          device, BF16 [T, Hq, D], 16-byte aligned
+ *   workspace    device, >= plan.workspace_bytes, 256-byte aligned (may be NULL
+ *                when that is 0)
+ * A block-table entry outside [0, N) that a row needs makes that row NaN; no
+ * out-of-bounds access happens for any device data. Values inside a context
+ * that a row does not see causally can still reach it if they are not finite
+ * (0 * inf in the weighted sum of V). Bit-identical from run to run. */
+pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, const int32_t* query_start,
+                            float scale, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

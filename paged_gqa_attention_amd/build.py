@@ -21,8 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["decode_kernels.hip", "kv_write.hip", "api.cpp"]
-HEADERS = ["launch.h"]
+SOURCES = ["decode_kernels.hip", "mq_kernels.hip", "kv_write.hip", "api.cpp"]
+HEADERS = ["launch.h", "device_common.h"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated (the host pass

@@ -79,6 +79,59 @@ pa_status_t make_plan(const pa_shape_t* s, pa_plan_t* p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+pa_status_t check_mq_shape(const pa_mq_shape_t* s) {
+  if (!s) return PA_ERR_NULL_POINTER;
+  if (s->batch < 0 || s->num_tokens < 0 || s->max_query_len < 1 || s->num_q_heads < 1 ||
+      s->num_kv_heads < 1 || s->head_dim < 1 || s->page_size < 1 || s->max_pages_per_seq < 1 ||
+      s->num_pages < 1 || s->split_pages < 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (s->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+  if (s->head_dim != 128 && s->head_dim != 256) return PA_ERR_UNSUPPORTED;
+  const int64_t g = s->num_q_heads / s->num_kv_heads;
+  // rows of one (sequence, KV head) and of the whole call fit 32-bit indices
+  if (g > PA_MAX_GQA_RATIO || s->batch > 65535 || s->num_kv_heads > 4096 ||
+      s->max_pages_per_seq > (1 << 20) || (int64_t)s->max_query_len * g > (1 << 24) ||
+      (int64_t)s->num_tokens * s->num_q_heads > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+struct MqPlan {
+  pa_plan_t plan;
+  int row_tiles, row_blocks;
+};
+
+pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
+  const int g = s->num_q_heads / s->num_kv_heads;
+  const int rows = s->max_query_len * g;  // rows of one (sequence, KV head)
+  const int rt = pa::mq_row_tiles(rows);
+  const int row_blocks = (rows + 16 * rt - 1) / (16 * rt);
+  const int w = s->max_pages_per_seq;
+  const int64_t base = (int64_t)(s->batch > 0 ? s->batch : 1) * s->num_kv_heads * row_blocks;
+  int pps;
+  if (s->split_pages > 0) {
+    pps = s->split_pages;
+  } else {
+    // split the context only while the rows alone give too few workgroups
+    const int64_t splits_wanted = (kTargetWorkgroups + base - 1) / base;
+    pps = (int)((w + splits_wanted - 1) / splits_wanted);
+  }
+  if (pps > w) pps = w;
+  if (pps < 1) pps = 1;
+  const int splits = (w + pps - 1) / pps;
+  if (base * splits > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const size_t parts = (size_t)s->num_tokens * s->num_q_heads * splits;
+  p->plan.split_pages = pps;
+  p->plan.num_splits = splits;
+  p->plan.workspace_bytes = splits == 1 ? 0
+                                        : align_up(parts * s->head_dim * sizeof(float), 256) +
+                                              align_up(parts * 2 * sizeof(float), 256);
+  p->row_tiles = rt;
+  p->row_blocks = row_blocks;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,6 +327,72 @@ pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, con
   a.num_pages = shape->num_pages;
   a.stream = stream;
   return pa::launch_kv_write(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status_t pa_mq_plan(const pa_mq_shape_t* shape, pa_plan_t* plan) {
+  if (!plan) return PA_ERR_NULL_POINTER;
+  const pa_status_t st = check_mq_shape(shape);
+  if (st != PA_OK) return st;
+  MqPlan p;
+  const pa_status_t pst = make_mq_plan(shape, &p);
+  if (pst == PA_OK) *plan = p.plan;
+  return pst;
+}
+
+pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, const int32_t* query_start,
+                            float scale, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  pa_status_t st = check_mq_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0 || shape->num_tokens == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !query_start || !out)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      ((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)query_start & 3u))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  MqPlan p;
+  st = make_mq_plan(shape, &p);
+  if (st != PA_OK) return st;
+  if (p.plan.workspace_bytes > 0) {
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.plan.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const size_t parts = (size_t)shape->num_tokens * shape->num_q_heads * p.plan.num_splits;
+  pa::MqLaunchArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = static_cast<uint16_t*>(out);
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = p.plan.workspace_bytes > 0
+                ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align_up(parts * shape->head_dim * sizeof(float), 256))
+                : nullptr;
+  a.batch = shape->batch;
+  a.num_tokens = shape->num_tokens;
+  a.max_query_len = shape->max_query_len;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  a.row_tiles = p.row_tiles;
+  a.row_blocks = p.row_blocks;
+  a.split_pages = p.plan.split_pages;
+  a.num_splits = p.plan.num_splits;
+  a.score_scale = scale * 1.4426950408889634f;
+  a.stream = stream;
+  if (pa::launch_mq(a) != 0) return PA_ERR_LAUNCH;
+  if (a.num_splits == 1) return PA_OK;
+  return pa::launch_mq_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -1,0 +1,151 @@
+// Device helpers shared by the decode, multi-query and merge kernels: BF16 and
+// FP8 conversions, the register software pipeline and the log-sum-exp merge of
+// split partials. Included by the .hip sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// BF16 -> FP32 is exact: the BF16 bits are the high half of the FP32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 -> BF16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// FP8 E4M3 (OCP) -> FP32 for the 4 codes of a word, with gfx950's
+// v_cvt_pk_f32_fp8 (exact: every E4M3 value is an FP32 value).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+}
+
+// 8 FP8 codes (2 words) -> 8 BF16 values packed for an MFMA operand. Exact:
+// E4M3 values have 3 mantissa bits and exponents within BF16's range, so the
+// FP32 value's upper half is the BF16 value.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  float f[8];
+  fp8x4_to_f32(w0, f);
+  fp8x4_to_f32(w1, f + 4);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+  return r;
+}
+
+// Software pipeline over n items held in NB register slots (item i in slot
+// i % NB): items i+1 .. i+NB-1 are loading while item i is used. In the steady
+// state every prefetch is issued unconditionally and pinned before the use
+// with a scheduling barrier, so the compiler's wait counts let exactly the
+// consumed item's loads complete; the tail (< 2*NB-1 items) guards each one.
+// `load(item, slot)` and `use(item, slot)` receive compile-time slot indices
+// after unrolling.
+template <int NB, class Load, class Use>
+__device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i)
+    if (i < n) load(i, i);
+  int j = 0;
+  for (; j + 2 * NB - 2 < n; j += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      load(j + u + NB - 1, (u + NB - 1) % NB);
+      __builtin_amdgcn_sched_barrier(0);
+      use(j + u, u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * NB - 2; ++u) {
+    if (j + u < n) {
+      if (j + u + NB - 1 < n) load(j + u + NB - 1, (u + NB - 1) % NB);
+      use(j + u, u % NB);
+    }
+  }
+}
+
+// Log-sum-exp merge of the first nv split partials of one (sequence, query
+// head) row, for the 4 dims d4 .. d4+3: M = max m_s, out = sum 2^(m_s-M) acc_s
+// / sum 2^(m_s-M) l_s. The partials of up to kMergeChunk splits are loaded
+// together, then folded into a running state, so a row costs one memory round
+// trip for the usual split counts. nv == 0 (empty context) gives zeros.
+constexpr int kMergeChunk = 8;
+
+template <int D>
+__device__ __forceinline__ f32x4 merge_row(const float* __restrict__ ws_acc,
+                                           const float* __restrict__ ws_ml, size_t row,
+                                           int num_splits, int nv, int d4) {
+  const float* ml = ws_ml + row * num_splits * 2;
+  const float* acc = ws_acc + row * num_splits * D + d4;
+  float m_run = -INFINITY, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nv; s0 += kMergeChunk) {
+    float2 mlv[kMergeChunk];
+    f32x4 av[kMergeChunk];
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      if (s0 + i < nv) {
+        mlv[i] = *reinterpret_cast<const float2*>(ml + 2 * (s0 + i));
+        av[i] = *reinterpret_cast<const f32x4*>(acc + (size_t)(s0 + i) * D);
+      }
+    }
+    float mc = m_run;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+      if (s0 + i < nv) mc = fmaxf(mc, mlv[i].x);
+    const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mc);
+    den *= a;
+    num *= a;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      if (s0 + i < nv) {
+        const float w = fast_exp2(mlv[i].x - mc);
+        den = fmaf(w, mlv[i].y, den);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] = fmaf(w, av[i][e], num[e]);
+      }
+    }
+    m_run = mc;
+  }
+  f32x4 res = {0.f, 0.f, 0.f, 0.f};
+  if (nv > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = num[e] / den;
+  }
+  return res;
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 v) {
+  uint2 packed;
+  packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = packed;
+}
+
+}  // namespace
+}  // namespace pa

@@ -51,4 +51,32 @@ struct KvWriteArgs {
 // Enqueue the KV write kernel; 0 on success, else the HIP error code.
 int launch_kv_write(const KvWriteArgs& a);
 
+// Arguments of a multi-query call, already validated on the host.
+struct MqLaunchArgs {
+  const uint16_t* q;           // bf16 [T, Hq, D]
+  const uint16_t* k_cache;     // bf16 [N, P, Hkv, D]
+  const uint16_t* v_cache;     // bf16 [N, P, Hkv, D]
+  const int32_t* block_table;  // int32 [B, W]
+  const int32_t* context_lens; // int32 [B]
+  const int32_t* query_start;  // int32 [B + 1]
+  uint16_t* out;               // bf16 [T, Hq, D]
+  float* ws_acc;               // f32 [T, Hq, S, D] (num_splits > 1 only)
+  float* ws_ml;                // f32 [T, Hq, S, 2]
+  int batch, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim;
+  int max_pages, num_pages;
+  int row_tiles;               // 16-row tiles per workgroup: 1, 2 or 4
+  int row_blocks;              // workgroups along the rows of one (sequence, KV head)
+  int split_pages, num_splits;
+  float score_scale;           // scale * log2(e)
+  void* stream;                // hipStream_t
+};
+
+// Row tiles per workgroup for a given number of rows per (sequence, KV head).
+int mq_row_tiles(int rows_per_head);
+
+// Enqueue the multi-query kernel (output, or split partials when
+// num_splits > 1) or the merge of its partials; 0 or the HIP error code.
+int launch_mq(const MqLaunchArgs& a);
+int launch_mq_reduce(const MqLaunchArgs& a);
+
 }  // namespace pa

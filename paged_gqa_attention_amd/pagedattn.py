@@ -6,8 +6,10 @@ ABI declared in ``include/pagedattn.h`` through ctypes, on torch's current
 stream. Every step of the computation runs in the library's HIP kernels; if
 the library is missing, importing the binding raises instead of falling back.
 
-Names follow the C ABI: ``pa_decode``, ``pa_plan``, ``pa_workspace_size``,
-``pa_status_string``, ``pa_abi_version``.
+Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_plan``,
+``pa_workspace_size``, ``pa_decode_partials``, ``pa_merge_partials``,
+``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_status_string``,
+``pa_abi_version``.
 """
 
 from __future__ import annotations
@@ -62,6 +64,21 @@ class PaKvWriteShape(ctypes.Structure):
     ]
 
 
+class PaMqShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("max_query_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("split_pages", ctypes.c_int32),
+    ]
+
+
 class PagedAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -109,6 +126,14 @@ def _load():
     lib.pa_kv_write.argtypes = [
         ctypes.POINTER(PaKvWriteShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.pa_mq_plan.restype = ctypes.c_int
+    lib.pa_mq_plan.argtypes = [ctypes.POINTER(PaMqShape), ctypes.POINTER(PaPlan)]
+    lib.pa_mq_attention.restype = ctypes.c_int
+    lib.pa_mq_attention.argtypes = [
+        ctypes.POINTER(PaMqShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
     ]
     return lib
 
@@ -328,3 +353,70 @@ def pa_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Te
                           _stream(k_new.device))
     if st != PA_OK:
         raise PagedAttnError(st, "pa_kv_write")
+
+
+def mq_shape_of(q, k_cache, block_table, max_query_len: int, split_pages: int = 0) -> PaMqShape:
+    T, Hq, D = q.shape
+    N, P, Hkv, _ = k_cache.shape
+    return PaMqShape(int(block_table.shape[0]), int(T), int(max_query_len), int(Hq), int(Hkv),
+                     int(D), int(P), int(block_table.shape[1]), int(N), int(split_pages))
+
+
+def pa_mq_plan(shape: PaMqShape) -> PaPlan:
+    plan = PaPlan()
+    st = _lib.pa_mq_plan(ctypes.byref(shape), ctypes.byref(plan))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_mq_plan")
+    return plan
+
+
+def pa_mq_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_table: torch.Tensor, context_lens: torch.Tensor,
+                    query_start: torch.Tensor, max_query_len: int,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    split_pages: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal multi-query attention over a paged BF16 cache; returns ``out`` [T, Hq, D].
+
+    q [T, Hq, D] bf16 packs the query tokens of all sequences token-major;
+    sequence b owns rows query_start[b] .. query_start[b+1]-1 (query_start
+    [B+1] int32 on the GPU), which are the last tokens of its context_lens[b]
+    cached tokens. ``max_query_len`` bounds every sequence's row count (a host
+    integer, as the launch is sized from it).
+    """
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [T,Hq,D] and k_cache == v_cache shape [N,P,Hkv,D]")
+    T, Hq, D = q.shape
+    if k_cache.shape[3] != D:
+        raise ValueError("head_dim of q and of the caches differ")
+    B = block_table.shape[0] if block_table.dim() == 2 else -1
+    if B < 0 or context_lens.shape != (B,) or query_start.shape != (B + 1,):
+        raise ValueError("expected block_table [B, W], context_lens [B], query_start [B+1]")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, torch.bfloat16),
+                        ("v_cache", v_cache, torch.bfloat16),
+                        ("block_table", block_table, torch.int32),
+                        ("context_lens", context_lens, torch.int32),
+                        ("query_start", query_start, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU of q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    shape = mq_shape_of(q, k_cache, block_table, max_query_len, split_pages)
+    plan = pa_mq_plan(shape)
+    if workspace is None and plan.workspace_bytes > 0:
+        workspace = _workspace(q.device, plan.workspace_bytes)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.pa_mq_attention(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
+                              v_cache.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
+                              query_start.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
+                              ws_ptr, ws_bytes, _stream(q.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_mq_attention")
+    return out

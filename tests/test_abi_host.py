@@ -28,13 +28,14 @@ fake_pointers = pytest.mark.skipif(torch.cuda.device_count() > 0,
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert names == ["pa_abi_version", "pa_decode", "pa_decode_partials", "pa_kv_write",
-                     "pa_merge_partials", "pa_plan", "pa_status_string", "pa_workspace_size"]
+    assert names == ["pa_abi_version", "pa_decode", "pa_decode_fp8", "pa_decode_partials",
+                     "pa_kv_write", "pa_merge_partials", "pa_mq_attention", "pa_mq_plan",
+                     "pa_plan", "pa_status_string", "pa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -204,3 +205,85 @@ def test_kv_write_rejects_bad_arguments():
         a[i] = bad
         assert call(good(), *a) == pa.PA_ERR_INVALID_ARGUMENT, i
     assert call(pa.PaKvWriteShape(0, 8, 128, 128, 64), None, None, None, None, None, None) == pa.PA_OK
+
+
+# ---- multi-query entry points ------------------------------------------------
+
+def _mq(B=16, T=64, L=4, Hq=40, Hkv=8, D=128, W=32, N=512, sp=0):
+    return pa.PaMqShape(B, T, L, Hq, Hkv, D, 128, W, N, sp)
+
+
+def test_mq_shape_struct():
+    assert ctypes.sizeof(pa.PaMqShape) == 10 * 4
+
+
+@pytest.mark.parametrize("kw,expect", [
+    # 4 query tokens x G 5 = 20 rows -> 2 row tiles, one row block; 128 workgroups
+    # want 4 splits of 8 pages
+    (dict(), (8, 4)),
+    # 512-token chunks: 2560 rows -> 40 row blocks of 64; 1280 workgroups: one split
+    (dict(B=4, T=2048, L=512), (32, 1)),
+    # (16, 2) head_dim 256, 257 rows x G 8 = 2056 rows -> 33 row blocks; B=4: 264
+    # workgroups want 2 splits
+    (dict(B=4, T=1028, L=257, Hq=16, Hkv=2, D=256, N=128), (16, 2)),
+    # one query row: decode-sized launch, 32 splits of 1 page
+    (dict(B=2, T=2, L=1, Hq=16, Hkv=2, D=256), (1, 32)),
+    # explicit split_pages is kept (clamped to W)
+    (dict(sp=3), (3, 11)),
+    (dict(sp=99), (32, 1)),
+])
+def test_mq_plan(kw, expect):
+    s = _mq(**kw)
+    plan = pa.pa_mq_plan(s)
+    assert (plan.split_pages, plan.num_splits) == expect
+    S = plan.num_splits
+    parts = s.num_tokens * s.num_q_heads * S
+    want = 0 if S == 1 else (-(-parts * s.head_dim * 4 // 256) * 256 + -(-parts * 8 // 256) * 256)
+    assert plan.workspace_bytes == want
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", -1, 2), ("num_tokens", -1, 2), ("max_query_len", 0, 2), ("num_q_heads", 0, 2),
+    ("num_kv_heads", 3, 2), ("head_dim", 64, 3), ("page_size", 64, 3),
+    ("max_pages_per_seq", 0, 2), ("num_pages", 0, 2), ("split_pages", -1, 2),
+    ("num_q_heads", 8 * 17, 3), ("max_query_len", 1 << 22, 3), ("batch", 70000, 3),
+])
+def test_mq_invalid_shapes(field, value, code):
+    s = _mq()
+    setattr(s, field, value)
+    assert pa.lib.pa_mq_plan(ctypes.byref(s), ctypes.byref(pa.PaPlan())) == code
+    d = 1 << 20
+    assert pa.lib.pa_mq_attention(ctypes.byref(s), d, d, d, d, d, d, ctypes.c_float(0.1), d,
+                                  d, 1 << 30, None) == code
+
+
+def test_mq_empty_calls_are_no_ops():
+    for s in (_mq(B=0), _mq(T=0)):
+        assert pa.lib.pa_mq_attention(ctypes.byref(s), None, None, None, None, None, None,
+                                      ctypes.c_float(0.1), None, None, 0, None) == pa.PA_OK
+
+
+@fake_pointers
+def test_mq_rejects_bad_pointers():
+    d = 1 << 20
+    s = _mq()
+    plan = pa.pa_mq_plan(s)
+    ok = [d, d, d, d, d, d, ctypes.c_float(0.1), d, d, plan.workspace_bytes, None]
+    assert pa.lib.pa_mq_plan(None, ctypes.byref(pa.PaPlan())) == pa.PA_ERR_NULL_POINTER
+    assert pa.lib.pa_mq_plan(ctypes.byref(s), None) == pa.PA_ERR_NULL_POINTER
+    assert pa.lib.pa_mq_attention(None, *ok) == pa.PA_ERR_NULL_POINTER
+    for i in (0, 1, 2, 3, 4, 5, 7, 8):
+        a = list(ok)
+        a[i] = None
+        assert pa.lib.pa_mq_attention(ctypes.byref(s), *a) == pa.PA_ERR_NULL_POINTER, i
+    for i, bad in ((0, d + 2), (1, d + 8), (2, d + 4), (3, d + 2), (4, d + 1), (5, d + 2),
+                   (7, d + 8), (8, d + 128)):
+        a = list(ok)
+        a[i] = bad
+        assert pa.lib.pa_mq_attention(ctypes.byref(s), *a) == pa.PA_ERR_INVALID_ARGUMENT, i
+    a = list(ok)
+    a[6] = ctypes.c_float(float("nan"))
+    assert pa.lib.pa_mq_attention(ctypes.byref(s), *a) == pa.PA_ERR_INVALID_ARGUMENT
+    a = list(ok)
+    a[9] = plan.workspace_bytes - 1
+    assert pa.lib.pa_mq_attention(ctypes.byref(s), *a) == pa.PA_ERR_WORKSPACE_TOO_SMALL

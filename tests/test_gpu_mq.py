@@ -1,0 +1,238 @@
+"""GPU parity of causal multi-query attention (pa_mq_attention) against the
+FP64 oracle: chunked prefill and multi-token decode over the paged cache."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import announce, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    from paged_gqa_attention_amd import pagedattn  # noqa: F401
+
+
+def run_mq(w, split_pages=0, max_query_len=None, out=None, scale=None):
+    from paged_gqa_attention_amd import pagedattn as pa
+    o = None if out is None else out.to(DEV)
+    res = pa.pa_mq_attention(w.q.to(DEV), w.k_cache.to(DEV), w.v_cache.to(DEV),
+                             w.block_table.to(DEV), w.context_lens.to(DEV),
+                             w.query_start.to(DEV),
+                             w.max_query_len if max_query_len is None else max_query_len,
+                             scale=w.scale if scale is None else scale, out=o,
+                             split_pages=split_pages)
+    torch.cuda.synchronize()
+    return res.cpu()
+
+
+def oracle_mq(w, scale=None):
+    return oracle.paged_multi_query_attention(w.q, w.k_cache, w.v_cache, w.block_table,
+                                              w.context_lens, w.query_start,
+                                              w.scale if scale is None else scale)
+
+
+def oracle_rows(w, tokens):
+    """Oracle outputs of selected packed token rows, one at a time: row i of a
+    chunk of Lq rows is single-query attention over the first ctx - Lq + i + 1
+    tokens."""
+    qs = w.query_start.tolist()
+    res = []
+    for t in tokens:
+        b = max(i for i in range(len(qs) - 1) if qs[i] <= t and t < qs[i + 1])
+        lq = qs[b + 1] - qs[b]
+        n = int(w.context_lens[b]) - lq + (t - qs[b]) + 1
+        res.append(oracle.paged_decode_attention(
+            w.q[t:t + 1], w.k_cache, w.v_cache, w.block_table[b:b + 1],
+            torch.tensor([max(n, 0)], dtype=torch.int32), w.scale)[0])
+    return np.stack(res)
+
+
+def test_small_mixed_chunks():
+    announce("mq small mixed chunks")
+    w = workloads.build_mq([4, 1, 7], [9, 128, 300], 40, 8, 128, seed=1, max_pages=3,
+                           pool="packed")
+    assert_parity(run_mq(w), oracle_mq(w), "mq small")
+
+
+@pytest.mark.parametrize("split_pages", [1, 2, 3, 8])
+def test_splits_agree_with_oracle(split_pages):
+    announce(f"mq splits {split_pages}")
+    w = workloads.build_mq([3, 16, 40, 1], [2051, 700, 1000, 4096], 40, 8, 128, seed=2,
+                           max_pages=32, pool="packed")
+    w = workloads.poison_unused(w)
+    assert_parity(run_mq(w, split_pages=split_pages), oracle_mq(w), f"mq sp{split_pages}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 12, 16])
+@pytest.mark.parametrize("D", [128, 256])
+def test_head_ratios_and_dims(G, D):
+    announce(f"mq G={G} D={D}")
+    w = workloads.build_mq([5, 2, 33], [130, 2, 257], 2 * G, 2, D, seed=10 * G + D,
+                           max_pages=3, pool="packed")
+    assert_parity(run_mq(w), oracle_mq(w), f"mq G{G} D{D}")
+
+
+@pytest.mark.parametrize("rows", [1, 16, 17, 32, 33, 64, 65, 257])
+def test_row_tile_boundaries(rows):
+    # rows per (sequence, KV head) = Lq * G crosses the 16 / 32 / 64 row tiles
+    announce(f"mq rows {rows}")
+    w = workloads.build_mq([rows, max(1, rows // 2)], [rows + 100, 700], 8, 8, 128,
+                           seed=rows, max_pages=6, pool="packed")
+    assert_parity(run_mq(w), oracle_mq(w), f"mq rows {rows}")
+
+
+def test_qwen_mtp4_full_size():
+    w = workloads.mq_config("mtp4")
+    announce("mq mtp4 full size")
+    assert_parity(run_mq(w), oracle_mq(w), "mq mtp4")
+
+
+@pytest.mark.parametrize("name", ["prefill512", "wide257"])
+def test_prefill_full_size_sampled_rows(name):
+    w = workloads.mq_config(name)
+    announce(f"mq {name} full size")
+    out = run_mq(w)
+    assert torch.isfinite(out.float()).all()
+    gen = torch.Generator().manual_seed(5)
+    qs = w.query_start.tolist()
+    # first and last row of every chunk plus random rows
+    toks = sorted(set([qs[b] for b in range(len(qs) - 1)] + [qs[b + 1] - 1 for b in range(len(qs) - 1)]
+                      + torch.randint(0, w.num_tokens, (24,), generator=gen).tolist()))
+    assert_parity(out[toks], oracle_rows(w, toks), f"mq {name} sampled")
+
+
+def test_wide_head_single_and_257_rows():
+    # the local (16, 2) head shape at 1 and 257 query rows, head_dim 256
+    for lq in (1, 257):
+        announce(f"mq (16,2) D256 lq={lq}")
+        w = workloads.build_mq([lq, lq], [2051, 300], 16, 2, 256, seed=lq, max_pages=17,
+                               pool="packed",
+                               scale=float(torch.tensor(1 / 16, dtype=torch.float32)))
+        assert_parity(run_mq(w), oracle_mq(w), f"mq wide lq{lq}")
+
+
+def test_single_query_rows_match_decode_oracle():
+    announce("mq lq=1 == decode")
+    w = workloads.build_mq([1] * 6, [1, 127, 128, 129, 1000, 4096], 40, 8, 128, seed=3,
+                           max_pages=32, pool="packed")
+    ref = oracle.paged_decode_attention(w.q, w.k_cache, w.v_cache, w.block_table,
+                                        w.context_lens, w.scale)
+    assert_parity(run_mq(w), ref, "mq lq1")
+
+
+def test_fully_masked_rows_are_zero_and_empty_chunks():
+    # sequence 1 has ctx 2 < Lq 5: its first 3 rows see nothing; sequence 2 has
+    # no query rows; sequence 0 is a first chunk (ctx == Lq)
+    announce("mq masked rows")
+    w = workloads.build_mq([6, 5, 0, 3], [6, 2, 50, 3], 40, 8, 128, seed=4, max_pages=1,
+                           pool="packed")
+    out = run_mq(w)
+    assert torch.all(out[6:9] == 0)
+    assert_parity(out, oracle_mq(w), "mq masked")
+
+
+def test_max_query_len_larger_than_needed_and_uncovered_rows():
+    announce("mq loose max_query_len, uncovered rows")
+    w = workloads.build_mq([3, 2], [10, 300], 40, 8, 128, seed=6, max_pages=3, pool="packed")
+    # two extra packed rows after the last sequence: owned by no sequence
+    T = w.num_tokens
+    q2 = torch.cat([w.q, torch.randn(2, 40, 128).to(torch.bfloat16)])
+    w2 = workloads.MqWorkload(w.name, q2, w.k_cache, w.v_cache, w.block_table, w.context_lens,
+                              w.query_start, w.scale)
+    sentinel = torch.full(q2.shape, 7.0, dtype=torch.bfloat16)
+    out = run_mq(w2, max_query_len=100, out=sentinel)
+    assert torch.all(out[T:] == 7.0)
+    assert_parity(out[:T], oracle_mq(w), "mq loose")
+
+
+def test_bad_context_and_bad_page_rows():
+    announce("mq bad device data")
+    w = workloads.build_mq([4, 4, 4], [300, 300, 260], 40, 8, 128, seed=7, max_pages=3,
+                           pool="packed")
+    ctx = w.context_lens.clone()
+    ctx[1] = 10 ** 6                        # out of range: sequence 1 is NaN
+    bt = w.block_table.clone()
+    bt[2, 2] = 10 ** 6                      # page 2 of sequence 2 (tokens 256..259) is bad
+    w2 = workloads.MqWorkload(w.name, w.q, w.k_cache, w.v_cache, bt, ctx, w.query_start, w.scale)
+    for sp in (1, 3):                       # three splits, then one (no merge kernel)
+        out = run_mq(w2, split_pages=sp).float()
+        ref = oracle_mq(w)
+        assert torch.isnan(out[4:8]).all()
+        # sequence 2: ctx 260, Lq 4 -> rows see 257..260 tokens; all touch page 2
+        assert torch.isnan(out[8:12]).all()
+        assert_parity(out[:4].to(torch.bfloat16), ref[:4], f"mq bad data sp{sp}")
+
+
+def test_bad_page_only_affects_rows_that_see_it():
+    announce("mq bad page, causal")
+    w = workloads.build_mq([4], [258], 40, 8, 128, seed=8, max_pages=3, pool="packed")
+    bt = w.block_table.clone()
+    bt[0, 2] = -5                         # tokens 256..257: seen by the last two rows only
+    w2 = workloads.MqWorkload(w.name, w.q, w.k_cache, w.v_cache, bt, w.context_lens,
+                              w.query_start, w.scale)
+    out = run_mq(w2).float()
+    ref = oracle_mq(w)
+    assert torch.isnan(out[2:]).all()
+    assert_parity(out[:2].to(torch.bfloat16), ref[:2], "mq bad page rows 0-1")
+
+
+def test_shared_prefix_pages():
+    # two sequences share their first pages (a common prefix), then diverge
+    announce("mq shared prefix")
+    w = workloads.build_mq([8, 8], [300, 400], 40, 8, 128, seed=9, max_pages=4,
+                           pool="permutation", num_pages=8)
+    bt = w.block_table.clone()
+    bt[1, 0] = bt[0, 0]
+    bt[1, 1] = bt[0, 1]
+    w2 = workloads.MqWorkload(w.name, w.q, w.k_cache, w.v_cache, bt, w.context_lens,
+                              w.query_start, w.scale)
+    assert_parity(run_mq(w2), oracle_mq(w2), "mq shared prefix")
+
+
+def test_deterministic_and_split_independent_of_stream():
+    announce("mq determinism")
+    w = workloads.build_mq([4] * 8, [4096] * 8, 40, 8, 128, seed=11, max_pages=32)
+    a = run_mq(w)
+    b = run_mq(w)
+    assert torch.equal(a, b)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = run_mq(w)
+    assert torch.equal(a, c)
+
+
+def test_graph_capture_replays():
+    announce("mq graph capture")
+    from paged_gqa_attention_amd import pagedattn as pa
+    w = workloads.build_mq([4] * 4, [1000, 2000, 3000, 4096], 40, 8, 128, seed=12, max_pages=32)
+    t = dict(q=w.q.to(DEV), k=w.k_cache.to(DEV), v=w.v_cache.to(DEV), bt=w.block_table.to(DEV),
+             ctx=w.context_lens.to(DEV), qs=w.query_start.to(DEV))
+    shape = pa.mq_shape_of(t["q"], t["k"], t["bt"], w.max_query_len)
+    plan = pa.pa_mq_plan(shape)
+    assert plan.num_splits > 1
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(t["q"])
+    eager = pa.pa_mq_attention(t["q"], t["k"], t["v"], t["bt"], t["ctx"], t["qs"],
+                               w.max_query_len, scale=w.scale, workspace=ws).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pa.pa_mq_attention(t["q"], t["k"], t["v"], t["bt"], t["ctx"], t["qs"],
+                               w.max_query_len, scale=w.scale, out=out, workspace=ws)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i

@@ -33,6 +33,7 @@ The five standard workloads follow the decode shapes of the pages: Qwen3-14B's
 
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass, field
 from typing import Optional, Sequence
@@ -198,12 +199,14 @@ def config(i: int) -> Workload:
 def poison_unused(w: Workload, value: float = float("nan")) -> Workload:
     """Fill every pool slot that no sequence reads with ``value`` (NaN default).
 
+    Works for decode (``Workload``) and multi-query (``MqWorkload``) inputs.
+
     The tail slots of each sequence's last page and every page no sequence
     uses are overwritten; slots that some sequence reads are left alone.
     """
-    P = w.page_size
-    used = torch.zeros(w.num_pages, P, dtype=torch.bool)
-    for b in range(w.batch):
+    N, P = int(w.k_cache.shape[0]), int(w.k_cache.shape[1])
+    used = torch.zeros(N, P, dtype=torch.bool)
+    for b in range(int(w.context_lens.numel())):
         n = int(w.context_lens[b])
         for j in range(-(-n // P)):
             page = int(w.block_table[b, j])
@@ -214,7 +217,7 @@ def poison_unused(w: Workload, value: float = float("nan")) -> Workload:
     v = w.v_cache.clone()
     k[mask] = value
     v[mask] = value
-    return Workload(w.name + "+poison", w.q, k, v, w.block_table, w.context_lens, w.scale, dict(w.meta))
+    return dataclasses.replace(w, name=w.name + "+poison", k_cache=k, v_cache=v)
 
 
 def fill_unused_table(w: Workload, value: int = -1) -> Workload:
@@ -257,3 +260,102 @@ def quantize_fp8(w: Workload) -> Fp8Pools:
     kc, ks = one(w.k_cache)
     vc, vs = one(w.v_cache)
     return Fp8Pools(kc, vc, ks, vs)
+
+
+# Multi-query (chunked prefill / multi-token decode) inputs --------------------
+
+@dataclass
+class MqWorkload:
+    """One multi-query call's inputs (CPU tensors).
+
+    q packs the query tokens of all sequences token-major: sequence b owns rows
+    query_start[b] .. query_start[b+1]-1, the last Lq_b of its ctx_b cached
+    tokens.
+    """
+
+    name: str
+    q: torch.Tensor             # bf16 [T, Hq, D]
+    k_cache: torch.Tensor       # bf16 [N, P, Hkv, D]
+    v_cache: torch.Tensor       # bf16 [N, P, Hkv, D]
+    block_table: torch.Tensor   # int32 [B, W]
+    context_lens: torch.Tensor  # int32 [B]
+    query_start: torch.Tensor   # int32 [B + 1]
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_query_len(self) -> int:
+        d = self.query_start[1:] - self.query_start[:-1]
+        return max(1, int(d.max())) if d.numel() else 1
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    def kv_bytes(self) -> int:
+        """K+V bytes the call must read at least once: sum(ctx) * Hkv * D * 4."""
+        return int(self.context_lens.to(torch.int64).sum()) * self.k_cache.shape[2] \
+            * self.k_cache.shape[3] * 4
+
+    def flops(self) -> int:
+        """Multiply-adds x 2 of q.K and P.V over every row's visible tokens."""
+        Hq, D = self.q.shape[1], self.q.shape[2]
+        total = 0
+        for b in range(self.context_lens.numel()):
+            lq = int(self.query_start[b + 1] - self.query_start[b])
+            ctx = int(self.context_lens[b])
+            for i in range(lq):
+                total += max(0, ctx - lq + i + 1)
+        return total * Hq * D * 4
+
+
+def build_mq(query_lens: Sequence[int], ctx: Sequence[int], Hq: int, Hkv: int, D: int, *,
+             seed: int, max_pages: Optional[int] = None, pool: str = "permutation",
+             num_pages: Optional[int] = None, scale: Optional[float] = None,
+             name: str = "mq", gen: Optional[torch.Generator] = None) -> MqWorkload:
+    """Build a multi-query workload: the cache as ``build`` draws it, then the
+    T = sum(query_lens) packed query rows (BF16-rounded standard normals)."""
+    if gen is None:
+        gen = torch.Generator().manual_seed(seed)
+    B = len(ctx)
+    assert len(query_lens) == B
+    w = build(B, Hq, Hkv, D, ctx, seed=seed, max_pages=max_pages, pool=pool,
+              num_pages=num_pages, scale=scale, name=name, gen=gen)
+    T = int(sum(query_lens))
+    q = _bf16_normal((T, Hq, D), gen)
+    qs = [0]
+    for n in query_lens:
+        qs.append(qs[-1] + int(n))
+    return MqWorkload(name, q, w.k_cache, w.v_cache, w.block_table, w.context_lens,
+                      torch.tensor(qs, dtype=torch.int32), w.scale,
+                      meta={"seed": seed, "pool": pool})
+
+
+MQ_DESCRIPTIONS = {
+    "mtp4": "multi-token decode: B=16, 4 query tokens each, ctx 4096, Hq=40, Hkv=8, D=128, "
+            "512-page shuffled pool",
+    "prefill512": "chunked prefill: B=4, 512-token chunks ending at ctx U[512,4096], Hq=40, Hkv=8, "
+                  "D=128, 128-page shuffled pool",
+    "wide257": "wide-head prefill: B=4, 257 query tokens each, ctx U[257,4096], Hq=16, Hkv=2, "
+               "D=256, 128-page shuffled pool, scale 1/16",
+}
+
+
+def mq_config(name: str) -> MqWorkload:
+    """Standard multi-query workloads (seeded by name)."""
+    seeds = {"mtp4": 2001, "prefill512": 2002, "wide257": 2003}
+    seed = seeds[name]
+    gen = torch.Generator().manual_seed(seed)
+    if name == "mtp4":
+        return build_mq([4] * 16, [MAX_CONTEXT] * 16, 40, 8, 128, seed=seed, gen=gen,
+                        max_pages=32, num_pages=512, name=name)
+    if name == "prefill512":
+        ctx = torch.randint(512, MAX_CONTEXT + 1, (4,), generator=gen).tolist()
+        return build_mq([512] * 4, ctx, 40, 8, 128, seed=seed, gen=gen, max_pages=32,
+                        num_pages=128, name=name)
+    if name == "wide257":
+        ctx = torch.randint(257, MAX_CONTEXT + 1, (4,), generator=gen).tolist()
+        return build_mq([257] * 4, ctx, 16, 2, 256, seed=seed, gen=gen, max_pages=32,
+                        num_pages=128, name=name,
+                        scale=float(torch.tensor(1.0 / 16.0, dtype=torch.float32)))
+    raise ValueError(name)
