@@ -105,7 +105,7 @@ struct MqPlan {
 pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
   const int g = s->num_q_heads / s->num_kv_heads;
   const int rows = s->max_query_len * g;  // rows of one (sequence, KV head)
-  const int rt = pa::mq_row_tiles(rows);
+  const int rt = pa::mq_row_tiles(rows, s->head_dim);
   const int row_blocks = (rows + 16 * rt - 1) / (16 * rt);
   const int w = s->max_pages_per_seq;
   const int64_t base = (int64_t)(s->batch > 0 ? s->batch : 1) * s->num_kv_heads * row_blocks;

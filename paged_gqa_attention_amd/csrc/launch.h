@@ -64,7 +64,7 @@ struct MqLaunchArgs {
   float* ws_ml;                // f32 [T, Hq, S, 2]
   int batch, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim;
   int max_pages, num_pages;
-  int row_tiles;               // 16-row tiles per workgroup: 1, 2 or 4
+  int row_tiles;               // 16-row tiles per workgroup: 1, 2, 4 or 8
   int row_blocks;              // workgroups along the rows of one (sequence, KV head)
   int split_pages, num_splits;
   float score_scale;           // scale * log2(e)
@@ -72,7 +72,7 @@ struct MqLaunchArgs {
 };
 
 // Row tiles per workgroup for a given number of rows per (sequence, KV head).
-int mq_row_tiles(int rows_per_head);
+int mq_row_tiles(int rows_per_head, int head_dim);
 
 // Enqueue the multi-query kernel (output, or split partials when
 // num_splits > 1) or the merge of its partials; 0 or the HIP error code.

@@ -10,11 +10,12 @@
 //
 // Work decomposition
 //   A row is one (query token, query head) pair of one KV head h: row r of
-//   sequence b and head h is token r / G, head h*G + r % G. mq_kernel<D,RT,KS>
+//   sequence b and head h is token r / G, head h*G + r % G. mq_kernel<D,RT>
 //   takes one workgroup per (sequence, KV head, block of 16*RT rows, split);
-//   its RT*KS waves are RT row tiles of 16 rows times KS KV streams. Each
-//   iteration stages KS consecutive 32-token chunks of K and V (one per
-//   stream) in LDS, and every wave then works on its stream's chunk:
+//   its waves split the RT row tiles of 16 rows (one or two per wave) and KS
+//   KV streams. Each iteration stages KS consecutive 32-token chunks of K and
+//   V (one per stream) in LDS, loaded into registers one or two iterations
+//   ahead, and every wave then works on its stream's chunk:
 //   1. S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (16 tokens x 16 rows per
 //      MFMA), so that lane (lq, lr) ends up with 8 scores of row lr: tokens
 //      4*lq + i and 16 + 4*lq + i of the chunk, i = 0..3.
@@ -45,21 +46,38 @@ namespace {
 
 constexpr int kMqPage = 128;   // tokens per page
 constexpr int kChunk = 32;     // tokens of one stream per iteration
+constexpr float kRescale = 8.f;  // lazy-rescaling threshold, log2 units
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef char __attribute__((address_space(3))) lds_char;
 
-// KV streams per workgroup for a row-tile count: 4 waves in all, except that
-// head_dim 256 with one row tile keeps to 2 streams (64 KiB of LDS).
+// Workgroup shapes, by RT = 16-row tiles per workgroup (1, 2, 4 or 8):
+//   TPW  row tiles per wave: 1, except 2 for head_dim 256 at RT 8 (its
+//        registers allow 4 waves of 32 rows, not 8 waves of 16); head_dim 128
+//        at RT 8 runs 8 waves (512 threads), so that every staged K/V chunk
+//        feeds 128 rows and the cache is re-read half as often as at RT 4
+//   WR   waves along the rows (RT / TPW)
+//   KS   KV streams, 4 waves in all (head_dim 256 always has RT >= 2)
+//   NBUF LDS stages: 2 (one barrier per iteration, the next stage is written
+//        while the current one is read) where both fit in 64 KiB, else 1
+//   PF   prefetch distance: the loads of iteration i + PF go out right after
+//        iteration i's registers are written to LDS (PF register slots)
+__host__ __device__ constexpr int mq_tpw(int d, int rt) { return rt == 8 && d == 256 ? 2 : 1; }
 __host__ __device__ constexpr int mq_streams(int d, int rt) {
-  return rt >= 4 ? 1 : (rt == 2 ? 2 : (d == 128 ? 4 : 2));
+  return rt >= 4 ? 1 : (rt == 2 ? 2 : 4);
 }
+__host__ __device__ constexpr int mq_waves(int d, int rt) {
+  return rt / mq_tpw(d, rt) * mq_streams(d, rt);
+}
+__host__ __device__ constexpr int mq_nbuf(int rt) { return rt >= 4 ? 2 : 1; }
+__host__ __device__ constexpr int mq_prefetch(int d, int rt) { return rt >= 4 && d == 128 ? 2 : 1; }
 
-// LDS bytes: K tiles of the KS streams, then their V tiles, each tile 32
-// token rows of 2*D bytes. The end-of-kernel stream merge reuses the space.
+// LDS bytes: per stage, the K tiles of the KS streams, then their V tiles,
+// each tile 32 token rows of 2*D bytes. The end-of-kernel stream merge reuses
+// the space.
 __host__ __device__ constexpr int mq_lds_bytes(int d, int rt) {
-  return 2 * mq_streams(d, rt) * kChunk * 2 * d;
+  return mq_nbuf(rt) * 2 * mq_streams(d, rt) * kChunk * 2 * d;
 }
 
 // 16-byte chunk c of token row r of a tile is stored at chunk position
@@ -75,14 +93,48 @@ __device__ __forceinline__ uint32_t v_off(int r, int c) {
   return (uint32_t)r * (2 * D) + 16u * (uint32_t)(c ^ ((r & 7) << 1));
 }
 
+// Loop over n iterations with PF register slots: iteration i's data is in
+// slot i % PF; body(i, slot) writes it to LDS, then calls issue(i + PF, slot)
+// through `next` (only while i + PF < n), then computes. In the steady state
+// every issue is unconditional, so the compiler's wait counts let exactly the
+// committed iteration's loads complete; the tail (< 2*PF iterations) guards
+// each one.
+//
+// The first PF issues are unconditional on the path into the steady-state
+// loop: if some path could enter the loop with fewer loads in flight, the
+// compiler would have to assume the youngest loads are the ones a commit
+// reads and wait for all of them.
+template <int PF, class Issue, class Body>
+__device__ __forceinline__ void staged_loop(int n, Issue&& issue, Body&& body) {
+  int j = 0;
+  if (n >= 2 * PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) issue(i, i);
+    for (; j + 2 * PF - 1 < n; j += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u)
+        body(j + u, u, [&]() { issue(j + u + PF, u); });
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (i < n) issue(i, i);
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * PF - 1; ++u) {
+    if (j + u < n)
+      body(j + u, u % PF, [&]() { if (j + u + PF < n) issue(j + u + PF, u % PF); });
+  }
+}
+
 __device__ __forceinline__ u32x2 lds_read_tr16(const lds_char* base, uint32_t off) {
   const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (v4i16 __attribute__((address_space(3)))*)(base + off));
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, int RT, int KS>
-__global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
+template <int D, int RT>
+__global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
@@ -90,26 +142,35 @@ __global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
     int batch, int num_tokens, int num_kv_heads, int gqa, int max_pages, int num_pages,
     int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale) {
   static_assert(D == 128 || D == 256, "head_dim");
-  constexpr int NT = 64 * RT * KS;          // threads
+  constexpr int TPW = mq_tpw(D, RT);
+  constexpr int WR = RT / TPW;
+  constexpr int KS = mq_streams(D, RT);
+  constexpr int NBUF = mq_nbuf(RT);
+  constexpr int PF = mq_prefetch(D, RT);
+  constexpr int NT = 64 * WR * KS;          // threads
   constexpr int ROWS = 16 * RT;             // rows per workgroup
   constexpr int KD = D / 32;                // k-steps of the score MFMA
   constexpr int DB = D / 16;                // 16-dim blocks of the output
   constexpr int CPR = D / 8;                // 16-byte chunks per token row
   constexpr int TILE = kChunk * 2 * D;      // bytes of one 32-token tile
+  constexpr int STAGE = 2 * KS * TILE;      // bytes of one LDS stage
   constexpr int UPT = 2 * KS * kChunk * CPR / NT;  // staged chunks per thread
   constexpr int IT = KS * kChunk;           // tokens per iteration
   static_assert(UPT * NT == 2 * KS * kChunk * CPR, "staging must tile evenly");
   static_assert(UPT % 2 == 0, "half K, half V");
-  static_assert(mq_lds_bytes(D, RT) == 2 * KS * TILE, "LDS size");
+  static_assert(KS == 1 || TPW == 1, "the stream merge handles one row tile per wave");
+  static_assert(mq_lds_bytes(D, RT) == NBUF * STAGE, "LDS size");
 
   extern __shared__ __attribute__((aligned(16))) char smem_mq[];
   lds_char* lds = (lds_char*)smem_mq;
 
   // 1-D grid, (sequence, KV head) pair fastest, then row block, then split.
+  // Row blocks go from the last one down: later query tokens see more of the
+  // context, so the longest workgroups are dispatched first.
   const int num_pairs = batch * num_kv_heads;
   const int pair = blockIdx.x % num_pairs;
   const int rest = blockIdx.x / num_pairs;
-  const int rb = rest % row_blocks;
+  const int rb = row_blocks - 1 - rest % row_blocks;
   const int s = rest / row_blocks;
   const int h = pair % num_kv_heads;
   const int b = pair / num_kv_heads;
@@ -129,17 +190,10 @@ __global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rt = wave % RT;   // row tile
-  const int g = wave / RT;    // KV stream
+  const int rw = wave % WR;   // row wave: row tiles rw*TPW .. rw*TPW + TPW-1
+  const int g = wave / WR;    // KV stream
   const int lq = lane >> 4;
   const int lr = lane & 15;
-
-  // This lane's row (lr of the tile) and the tokens it may see.
-  const int row = row0 + 16 * rt + lr;
-  const bool row_ok = row < rows_b;
-  const int i_tok = row_ok ? row / gqa : 0;
-  const int hq = h * gqa + (row_ok ? row - i_tok * gqa : 0);
-  const size_t t_row = (size_t)qs0 + i_tok;  // packed token index of the row
 
   const int split_tokens = split_pages * kMqPage;
   const int t_begin = s * split_tokens;
@@ -147,18 +201,40 @@ __global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
   const int n_last = bad_ctx ? 0 : ctx - lqn + last_row / gqa + 1;
   const int t_end = min(t_begin + split_tokens, n_last);
   if (num_splits > 1 && (bad_ctx || t_end <= t_begin)) return;  // the merge skips it
-  const int n_row = ctx - lqn + i_tok + 1;
-  const int lim = row_ok ? min(n_row, t_end) : 0;  // tokens [t_begin, lim) are visible
+
+  // This lane's row in each of the wave's row tiles, and the tokens it sees:
+  // [t_begin, lim).
+  bool row_ok[TPW];
+  int lim[TPW];
+  size_t orow[TPW];  // row of q / out: packed token * Hq + query head
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int row = row0 + 16 * (rw * TPW + tt) + lr;
+    row_ok[tt] = row < rows_b;
+    const int i_tok = row_ok[tt] ? row / gqa : 0;
+    const int hq = h * gqa + (row_ok[tt] ? row - i_tok * gqa : 0);
+    orow[tt] = ((size_t)qs0 + i_tok) * num_q_heads + hq;
+    lim[tt] = row_ok[tt] ? min(ctx - lqn + i_tok + 1, t_end) : 0;
+  }
+
+  // Fewest visible tokens over the wave's real rows: chunks that end at or
+  // before it need no masking.
+  int lim_min = INT32_MAX;
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) lim_min = min(lim_min, row_ok[tt] ? lim[tt] : INT32_MAX);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   // B operand of the score MFMA: lane (lq, lr) holds dims 32*kk + 8*lq .. +7
   // of its row's q, the dims its K operand holds (zeros for rows past the end).
-  u32x4 qb[KD];
-  {
-    const uint16_t* qrow = q + (t_row * num_q_heads + hq) * D;
+  u32x4 qb[TPW][KD];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
-      qb[kk] = row_ok ? load16(qrow + 32 * kk + 8 * lq) : u32x4{0u, 0u, 0u, 0u};
-  }
+      qb[tt][kk] = row_ok[tt] ? load16(q + orow[tt] * D + 32 * kk + 8 * lq)
+                              : u32x4{0u, 0u, 0u, 0u};
 
   // ---- staging: chunk k of thread tid is unit u = tid + NT*k; units
   // [0, NT*UPT/2) are K, the rest V; in each half, unit -> (stream, row, chunk).
@@ -167,18 +243,17 @@ __global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
   const int32_t* bt_row = block_table + (size_t)b * max_pages;
   const int n_it = t_end > t_begin ? (t_end - t_begin + IT - 1) / IT : 0;
 
-  u32x4 stg[UPT];
-  int stg_tb = 0;        // first token of the staged iteration
-  bool stg_bad = false;  // its page id is outside the pool
+  u32x4 stg[PF][UPT];
+  bool stg_bad[PF];
   int next_page = n_it > 0 ? bt_row[t_begin / kMqPage] : 0;
 
-  auto issue = [&](int it) {
+  // Loads of iteration it (called in increasing it) into register slot `slot`.
+  auto issue = [&](int it, int slot) {
     const int tb = t_begin + it * IT;
     const int page = next_page;
     if (it + 1 < n_it) next_page = bt_row[(tb + IT) / kMqPage];
-    stg_tb = tb;
-    stg_bad = (unsigned)page >= (unsigned)num_pages;
-    const size_t base = (size_t)(stg_bad ? 0 : page) * page_elems + (size_t)h * D +
+    stg_bad[slot] = (unsigned)page >= (unsigned)num_pages;
+    const size_t base = (size_t)(stg_bad[slot] ? 0 : page) * page_elems + (size_t)h * D +
                         (size_t)(tb & (kMqPage - 1)) * row_elems;
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
@@ -186,10 +261,26 @@ __global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
       const int c = u % CPR;
       const int tr = u / CPR;  // token of the iteration: stream * 32 + row
       const uint16_t* pool = k < UPT / 2 ? k_cache : v_cache;
-      stg[k] = load16(pool + base + (size_t)tr * row_elems + 8 * c);
+      stg[slot][k] = load16(pool + base + (size_t)tr * row_elems + 8 * c);
     }
   };
-  auto commit = [&]() {
+  // Register slot -> LDS stage of iteration it.
+  auto commit = [&](int it, int slot) {
+    const int tb = t_begin + it * IT;
+    lds_char* stage = lds + (NBUF == 2 ? (it & 1) * STAGE : 0);
+    if (tb + IT <= t_end && !stg_bad[slot]) {  // the usual case: nothing to mask
+#pragma unroll
+      for (int k = 0; k < UPT; ++k) {
+        const bool is_k = k < UPT / 2;
+        const int u = (tid + NT * k) % (NT * UPT / 2);
+        const int c = u % CPR;
+        const int tr = u / CPR;
+        const uint32_t off = (is_k ? 0u : (uint32_t)(KS * TILE)) + (uint32_t)((tr / kChunk) * TILE) +
+                             (is_k ? k_off<D>(tr % kChunk, c) : v_off<D>(tr % kChunk, c));
+        *(u32x4 __attribute__((address_space(3)))*)(stage + off) = stg[slot][k];
+      }
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const bool is_k = k < UPT / 2;
@@ -198,157 +289,209 @@ __global__ __launch_bounds__(64 * RT * KS) void mq_kernel(
       const int tr = u / CPR;
       const int st = tr / kChunk;
       const int r = tr % kChunk;
-      u32x4 v = stg[k];
+      u32x4 v = stg[slot][k];
       // rows past the range hold other data (NaN poison included): zero them,
       // so that P = 0 times V stays 0. A bad page reads as NaN K (the rows
       // that see it become NaN) and zero V (the rows that do not see it are
       // unaffected).
-      if (stg_tb + tr >= t_end) v = u32x4{0u, 0u, 0u, 0u};
-      else if (stg_bad) v = is_k ? u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}
-                                 : u32x4{0u, 0u, 0u, 0u};
+      if (tb + tr >= t_end) v = u32x4{0u, 0u, 0u, 0u};
+      else if (stg_bad[slot]) v = is_k ? u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}
+                                       : u32x4{0u, 0u, 0u, 0u};
       const uint32_t off = (is_k ? 0u : (uint32_t)(KS * TILE)) + (uint32_t)(st * TILE) +
                            (is_k ? k_off<D>(r, c) : v_off<D>(r, c));
-      *(u32x4 __attribute__((address_space(3)))*)(lds + off) = v;
+      *(u32x4 __attribute__((address_space(3)))*)(stage + off) = v;
     }
   };
 
-  // ---- running state of the lane's row ------------------------------------
-  float m_run = -INFINITY;  // max of the log2-scaled scores seen
-  float l_run = 0.f;        // lane-local part of the sum of probabilities
-  f32x4 o[DB];              // O^T: lane (lq, lr) holds dims 16*db + 4*lq + i of row lr
+  // ---- running state of the lane's rows ------------------------------------
+  float m_run[TPW];  // max of the log2-scaled scores seen
+  float l_run[TPW];  // lane-local part of the sum of probabilities
+  f32x4 o[TPW][DB];  // O^T: lane (lq, lr) holds dims 16*db + 4*lq + i of row lr
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const lds_char* kt = lds + g * TILE;
-  const lds_char* vt = lds + KS * TILE + g * TILE;
+  for (int tt = 0; tt < TPW; ++tt) {
+    m_run[tt] = -INFINITY;
+    l_run[tt] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[tt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute = [&](int it) {
+    const lds_char* stage = lds + (NBUF == 2 ? (it & 1) * STAGE : 0);
+    const lds_char* kt = stage + g * TILE;
+    const lds_char* vt = stage + KS * TILE + g * TILE;
     const int tb = t_begin + it * IT + kChunk * g;  // first token of this stream's chunk
-    f32x4 sacc[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      sacc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        const u32x4 a =
-            *(const u32x4 __attribute__((address_space(3)))*)(kt + k_off<D>(16 * half + lr, 4 * kk + lq));
-        sacc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qb[kk]), sacc[half], 0, 0, 0);
-      }
-    }
-    // lane (lq, lr): sacc[half][i] = S[row lr][token tb + 16*half + 4*lq + i]
-    float sc[8];
-    float mx = -INFINITY;
+    // All LDS operand reads of the chunk go out first (K for the scores, then
+    // the V^T operands of the first VB dim blocks, which do not depend on the
+    // softmax), so their latency overlaps the MFMAs and the softmax instead
+    // of stalling each MFMA.
+    u32x4 ka[2][KD];
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tb + 16 * half + 4 * lq + i;
-        const float v = t < lim ? sacc[half][i] * score_scale : -INFINITY;
-        sc[4 * half + i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    f32x8 p;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = fast_exp2(sc[j] - m_use);
-    const bf16x8 pb = __builtin_convertvector(p, bf16x8);
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ps += (float)pb[j];  // the sum of the weights used
-    l_run = fmaf(l_run, alpha, ps);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      o[db] *= alpha;
-      // A operand: lane (lq, lr) gets V[token 4*lq + j][16*db + lr] (j < 4)
-      // and V[token 16 + 4*lq + j - 4][16*db + lr] (j >= 4).
+      for (int kk = 0; kk < KD; ++kk)
+        ka[half][kk] = *(const u32x4 __attribute__((address_space(3)))*)(
+            kt + k_off<D>(16 * half + lr, 4 * kk + lq));
+    // A operand of P.V, dim block db: lane (lq, lr) gets V[token 4*lq + j]
+    // [16*db + lr] (j < 4) and V[token 16 + 4*lq + j - 4][16*db + lr] (j >= 4).
+    auto read_v = [&](int db) -> u32x4 {
       const int c = 2 * db + ((lr & 3) >> 1);
       const uint32_t sub = 8u * (lr & 1);
       const u32x2 lo = lds_read_tr16(vt, v_off<D>(4 * lq + (lr >> 2), c) + sub);
       const u32x2 hi = lds_read_tr16(vt, v_off<D>(16 + 4 * lq + (lr >> 2), c) + sub);
-      const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[db],
-                                                      0, 0, 0);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    constexpr int VB = D == 128 ? DB : DB / 2;  // V blocks read ahead (register budget)
+    u32x4 va[VB];
+#pragma unroll
+    for (int db = 0; db < VB; ++db) va[db] = read_v(db);
+    f32x4 sacc[TPW][2];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+      sacc[tt][0] = sacc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+          sacc[tt][half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, ka[half][kk]), __builtin_bit_cast(bf16x8, qb[tt][kk]),
+              sacc[tt][half], 0, 0, 0);
+    // lane (lq, lr): sacc[tt][half][i] = S[row lr of tile tt][token tb + 16*half + 4*lq + i]
+    const bool full = tb + kChunk <= lim_min;  // wave-uniform: no token to mask
+    bf16x8 pb[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      float sc[8];
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sc[j] = sacc[tt][j >> 2][j & 3] * score_scale;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = tb + 16 * (j >> 2) + 4 * lq + (j & 3);
+          sc[j] = t < lim[tt] ? sacc[tt][j >> 2][j & 3] * score_scale : -INFINITY;
+        }
+      }
+      float lmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      // Lazy rescaling: the row's reference max m_run (the same on the row's
+      // four lanes) moves only when a score exceeds it by more than kRescale
+      // (log2 units), so probabilities stay below 2^kRescale and the
+      // accumulators are rescaled rarely. Each lane checks its own scores;
+      // only if one of them in the wave trips the check does the wave take
+      // the exact row max across lanes and rescale (a wave-uniform branch).
+      // Every term and the sum use the same reference: the result is the
+      // same softmax.
+      if (__builtin_amdgcn_ballot_w64(lmax > m_run[tt] + kRescale)) {
+        float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_ref = mx > m_run[tt] + kRescale ? mx : m_run[tt];  // same on the row
+        // 1 if the reference stays (also for a row with no visible token yet,
+        // where -inf - -inf would be NaN), 0 when it leaves -inf
+        const float alpha = m_ref == m_run[tt] ? 1.f : fast_exp2(m_run[tt] - m_ref);
+        l_run[tt] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[tt][db] *= alpha;
+        m_run[tt] = m_ref;
+      }
+      const float m_use = m_run[tt] == -INFINITY ? 0.f : m_run[tt];
+      f32x8 p;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(sc[j] - m_use);
+      pb[tt] = __builtin_convertvector(p, bf16x8);
+      l_run[tt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    // the remaining V blocks (head_dim 256) are read while the first ones multiply
+    u32x4 vb[DB - VB > 0 ? DB - VB : 1];
+#pragma unroll
+    for (int db = VB; db < DB; ++db) vb[db - VB] = read_v(db);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x4 a = db < VB ? va[db < VB ? db : 0] : vb[db >= VB ? db - VB : 0];
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+        o[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           pb[tt], o[tt][db], 0, 0, 0);
     }
   };
 
-  if (n_it > 0) issue(0);
-  for (int it = 0; it < n_it; ++it) {
-    __syncthreads();  // every wave is done with the previous tiles
-    commit();
-    if (it + 1 < n_it) issue(it + 1);
-    __syncthreads();
-    compute(it);
+  staged_loop<PF>(
+      n_it, [&](int it, int slot) { issue(it, slot); },
+      [&](int it, int slot, auto&& next) {
+        // with one stage, every wave must be done with the previous tiles
+        if constexpr (NBUF == 1) __syncthreads();
+        commit(it, slot);
+        next();
+        __syncthreads();
+        compute(it);
+      });
+
+  // the rows' sums over the 4 lane groups (same order on every lane)
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const float l1 = l_run[tt] + __shfl_xor(l_run[tt], 16);
+    l_run[tt] = l1 + __shfl_xor(l1, 32);
   }
 
-  // the row's sum over the 4 lane groups (same order on every lane)
-  {
-    const float l1 = l_run + __shfl_xor(l_run, 16);
-    l_run = l1 + __shfl_xor(l1, 32);
-  }
-
-  // ---- merge the KS streams of each row tile, in stream order ------------
+  // ---- merge the KS streams of each row wave, in stream order -------------
   if constexpr (KS > 1) {
-    constexpr int REC = 32 + 16 * D;  // floats per (row tile, stream): m, l, O^T
+    constexpr int REC = 32 + 16 * D;  // floats per (row wave, stream): m, l, O^T
     float* rec = (float*)smem_mq;
     __syncthreads();  // every wave is done with the tiles
     if (g > 0) {
-      float* my = rec + (size_t)((g - 1) * RT + rt) * REC;
+      float* my = rec + (size_t)((g - 1) * WR + rw) * REC;
       if (lq == 0) {
-        my[lr] = m_run;
-        my[16 + lr] = l_run;
+        my[lr] = m_run[0];
+        my[16 + lr] = l_run[0];
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) my[32 + (16 * db + 4 * lq + i) * 16 + lr] = o[db][i];
+        for (int i = 0; i < 4; ++i) my[32 + (16 * db + 4 * lq + i) * 16 + lr] = o[0][db][i];
     }
     __syncthreads();
     if (g > 0) return;
 #pragma unroll
     for (int gg = 1; gg < KS; ++gg) {
-      const float* ot = rec + (size_t)((gg - 1) * RT + rt) * REC;
+      const float* ot = rec + (size_t)((gg - 1) * WR + rw) * REC;
       const float m2 = ot[lr];
       const float l2 = ot[16 + lr];
-      const float m_new = fmaxf(m_run, m2);
+      const float m_new = fmaxf(m_run[0], m2);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float a1 = fast_exp2(m_run - m_use);
+      const float a1 = fast_exp2(m_run[0] - m_use);
       const float a2 = fast_exp2(m2 - m_use);
-      l_run = l_run * a1 + l2 * a2;
+      l_run[0] = l_run[0] * a1 + l2 * a2;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          o[db][i] = o[db][i] * a1 + ot[32 + (16 * db + 4 * lq + i) * 16 + lr] * a2;
-      m_run = m_new;
+          o[0][db][i] = o[0][db][i] * a1 + ot[32 + (16 * db + 4 * lq + i) * 16 + lr] * a2;
+      m_run[0] = m_new;
     }
   }
 
-  if (!row_ok) return;
-  const size_t orow = t_row * num_q_heads + hq;
-  if (num_splits == 1) {
-    if (bad_ctx) {
-      const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    if (!row_ok[tt]) continue;
+    if (num_splits == 1) {
+      uint16_t* dst = out + orow[tt] * D + 4 * lq;
+      if (bad_ctx) {
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int db = 0; db < DB; ++db) store_bf16x4(dst + 16 * db, f32x4{nan, nan, nan, nan});
+      } else {
+        const float inv = l_run[tt] > 0.f ? 1.f / l_run[tt] : 0.f;  // no visible token: zeros
+#pragma unroll
+        for (int db = 0; db < DB; ++db) store_bf16x4(dst + 16 * db, o[tt][db] * inv);
+      }
+    } else {
+      const size_t slot = orow[tt] * num_splits + s;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        store_bf16x4(out + orow * D + 16 * db + 4 * lq, f32x4{nan, nan, nan, nan});
-      return;
+        *reinterpret_cast<f32x4*>(ws_acc + slot * D + 16 * db + 4 * lq) = o[tt][db];
+      if (lq == 0) *reinterpret_cast<float2*>(ws_ml + slot * 2) = make_float2(m_run[tt], l_run[tt]);
     }
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;  // no visible token: zeros
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      store_bf16x4(out + orow * D + 16 * db + 4 * lq, o[db] * inv);
-  } else {
-    const size_t slot = orow * num_splits + s;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4*>(ws_acc + slot * D + 16 * db + 4 * lq) = o[db];
-    if (lq == 0) *reinterpret_cast<float2*>(ws_ml + slot * 2) = make_float2(m_run, l_run);
   }
 }
 
@@ -393,7 +536,6 @@ __global__ __launch_bounds__(256) void mq_reduce_kernel(
 
 template <int D, int RT>
 int launch_mq_drt(const MqLaunchArgs& a) {
-  constexpr int KS = mq_streams(D, RT);
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int gqa = a.num_q_heads / a.num_kv_heads;
   const dim3 grid(a.batch * a.num_kv_heads * a.row_blocks * a.num_splits);
@@ -404,16 +546,17 @@ int launch_mq_drt(const MqLaunchArgs& a) {
                   (void*)&gqa,           (void*)&a.max_pages,     (void*)&a.num_pages,
                   (void*)&a.max_query_len, (void*)&a.row_blocks,  (void*)&a.split_pages,
                   (void*)&a.num_splits,  (void*)&a.score_scale};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq_kernel<D, RT, KS>), grid,
-                              dim3(64 * RT * KS), args, mq_lds_bytes(D, RT), stream);
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq_kernel<D, RT>), grid,
+                              dim3(64 * mq_waves(D, RT)), args, mq_lds_bytes(D, RT), stream);
 }
 
 template <int D>
 int launch_mq_d(const MqLaunchArgs& a) {
   switch (a.row_tiles) {
-    case 1: return launch_mq_drt<D, 1>(a);
+    case 1: return D == 128 ? launch_mq_drt<128, 1>(a) : -1;
     case 2: return launch_mq_drt<D, 2>(a);
-    default: return launch_mq_drt<D, 4>(a);
+    case 4: return launch_mq_drt<D, 4>(a);
+    default: return launch_mq_drt<D, 8>(a);
   }
 }
 
@@ -434,7 +577,13 @@ int launch_mq_reduce_d(const MqLaunchArgs& a) {
 
 }  // namespace
 
-int mq_row_tiles(int rows_per_head) { return rows_per_head <= 16 ? 1 : (rows_per_head <= 32 ? 2 : 4); }
+int mq_row_tiles(int rows_per_head, int head_dim) {
+  // head_dim 256 starts at two row tiles: one row wave would stage 512 bytes
+  // of K/V per thread and iteration, more than its registers hold
+  const int min_rt = head_dim == 256 ? 2 : 1;
+  const int rt = rows_per_head <= 16 ? 1 : (rows_per_head <= 32 ? 2 : (rows_per_head <= 64 ? 4 : 8));
+  return rt < min_rt ? min_rt : rt;
+}
 
 int launch_mq(const MqLaunchArgs& a) {
   return a.head_dim == 128 ? launch_mq_d<128>(a) : launch_mq_d<256>(a);
