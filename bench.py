@@ -17,7 +17,8 @@ Printed: one JSON line with KV-read throughput (GB/s of K+V bytes the calls
 must read, whole job), the per-call time, the roofline of the partition
 kernel (timed alone with HIP events over the same rotation), the oracle timed
 on the host cores on a bounded sample, and per-call times of the other
-standard workloads.
+standard workloads (decode configs, FP8 pools, the paged KV write, and
+multi-query attention: multi-token decode and chunked prefill).
 """
 
 from __future__ import annotations
@@ -34,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 METRIC = "paged GQA decode attention: µs/call and KV-read GB/s (% of HBM peak)"
 KERNEL_SRC = os.path.join(ROOT, "paged_gqa_attention_amd", "csrc", "decode_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_kernel_config3_traffic.json")
@@ -88,12 +90,12 @@ def write_traffic(fetch_dir, write_dir):
     same run (1 GiB read, 1 GiB written), so the result is in true bytes.
     """
     import statistics
-    out = {"kernel": "partition_kernel<128, 5>", "workload": "batch 16 x 4096, 40/8 heads, D 128",
+    out = {"kernel": "partition_kernel<128, 5, false>", "workload": "batch 16 x 4096, 40/8 heads, D 128",
            "kernel_source_sha256_16": kernel_source_hash()}
     per = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, name)
-        part = [v for k, g, v in rows if "partition_kernel<128, 5>" in k]
+        part = [v for k, g, v in rows if "partition_kernel<128, 5, false>" in k]
         copy = [v for k, g, v in rows if "copy" in k.lower() and "partition" not in k
                 and "reduce" not in k]
         if not part or not copy:
@@ -262,7 +264,7 @@ def main():
             "kv_bytes_per_call": kv_bytes,
         },
         "roofline": {
-            "kernel": "partition_kernel<128,5>",
+            "kernel": "partition_kernel<128,5,false> (BF16 pools)",
             "bound": "hbm",
             "achieved": round(part_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -401,6 +403,40 @@ def main():
             }
             print(f"[bench] kv_write T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
         del kc, vc
+
+        # multi-query attention (multi-token decode, chunked prefill): cold
+        # rotation over 4 copies of each workload's cache
+        for name in ("mtp4", "prefill512", "wide257"):
+            wm = workloads.mq_config(name)
+            shp = pa.mq_shape_of(wm.q, wm.k_cache, wm.block_table, wm.max_query_len)
+            pl = pa.pa_mq_plan(shp)
+            wsx = torch.empty(max(256, pl.workspace_bytes), dtype=torch.uint8, device=dev)
+            btx, ctxx, qsx = (wm.block_table.to(dev), wm.context_lens.to(dev),
+                              wm.query_start.to(dev))
+            keep, margs = [], []
+            for _ in range(4):
+                qx, kx, vx = wm.q.to(dev), wm.k_cache.to(dev), wm.v_cache.to(dev)
+                ox = torch.empty_like(qx)
+                keep.append((qx, kx, vx, ox))
+                margs.append((ctypes.byref(shp), qx.data_ptr(), kx.data_ptr(), vx.data_ptr(),
+                              btx.data_ptr(), ctxx.data_ptr(), qsx.data_ptr(),
+                              ctypes.c_float(wm.scale), ox.data_ptr(), wsx.data_ptr(),
+                              wsx.numel(), stream))
+            ms = timed(torch, [lambda a=a: pa.lib.pa_mq_attention(*a) for a in margs], 100, 8)
+            by, fl = wm.kv_bytes(), wm.flops()
+            extra[f"mq_{name}"] = {
+                "description": workloads.MQ_DESCRIPTIONS[name],
+                "us_per_call": round(ms * 1e3, 2),
+                "kv_bytes_per_call": by,
+                "kv_gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                "flops_per_call": fl,
+                "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                "frac_of_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "split_pages": pl.split_pages, "num_splits": pl.num_splits,
+            }
+            print(f"[bench] mq {name}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+            del keep, margs, wsx
+            torch.cuda.empty_cache()
         result["other_workloads"] = extra
 
     if args.calibrate_copy:
