@@ -326,7 +326,10 @@ def main():
                 sets.append((qx, w.k_cache.to(dev), w.v_cache.to(dev), torch.empty_like(qx)))
             ds = [Decoder(pa, *s[:3], btx, ctxx, s[3], wsx, w.scale, shp, stream) for s in sets]
             steps = 200 if cfg != 4 else 60
-            ms = timed(torch, [d.decode for d in ds], steps, max(4, copies))
+            # the oracle's host-only phase lets the GPU clock down: launch-bound
+            # workload 1 gets a warm-up of ~20 ms before its timed calls
+            warm = 2000 if cfg == 1 else max(8, 2 * copies)
+            ms = timed(torch, [d.decode for d in ds], steps if cfg != 1 else 2000, warm)
             by = w.kv_bytes()
             extra[f"config{cfg}"] = {
                 "description": workloads.CONFIG_DESCRIPTIONS[cfg],
