@@ -17,3 +17,9 @@ from .decode import (  # noqa: F401
     paged_multi_query_attention,
     partial_attention,
 )
+from .prologue import (  # noqa: F401
+    attention_prologue,
+    rms_norm_heads,
+    rope_angles,
+    rope_neox,
+)
