@@ -17,8 +17,9 @@ Printed: one JSON line with KV-read throughput (GB/s of K+V bytes the calls
 must read, whole job), the per-call time, the roofline of the partition
 kernel (timed alone with HIP events over the same rotation), the oracle timed
 on the host cores on a bounded sample, and per-call times of the other
-standard workloads (decode configs, FP8 pools, the paged KV write, and
-multi-query attention: multi-token decode and chunked prefill).
+standard workloads (decode configs, FP8 pools, the paged KV write,
+multi-query attention: multi-token decode and chunked prefill, and the
+QK-norm/RoPE/KV-write prologue).
 """
 
 from __future__ import annotations
@@ -440,6 +441,34 @@ def main():
             print(f"[bench] mq {name}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
             del keep, margs, wsx
             torch.cuda.empty_cache()
+        # attention prologue (QK-norm, NeoX RoPE, KV write): a decode step's 16
+        # tokens (launch-bound) and an 8192-token prefill chunk (HBM-bound;
+        # per token q, k, v read once and q, K, V written once)
+        Hq, Hkv, D = 40, 8, 128
+        for T in (16, 8192):
+            gen = torch.Generator(device=dev).manual_seed(70 + T)
+            bfd = lambda *sz: torch.randn(*sz, device=dev, generator=gen).to(torch.bfloat16)
+            qx, kx, vx = bfd(T, Hq, D), bfd(T, Hkv, D), bfd(T, Hkv, D)
+            wq, wk = bfd(D), bfd(D)
+            kcx, vcx = bfd(512, 128, Hkv, D), bfd(512, 128, Hkv, D)
+            posx = torch.arange(T, device=dev, dtype=torch.int32)
+            slx = torch.randperm(512 * 128, device=dev, generator=gen)[:T].to(torch.int32)
+            qox = torch.empty_like(qx)
+            pshape = pa.PaPrologueShape(T, Hq, Hkv, D, 128, 512)
+            pargs = (ctypes.byref(pshape), qx.data_ptr(), kx.data_ptr(), vx.data_ptr(),
+                     wq.data_ptr(), wk.data_ptr(), posx.data_ptr(), slx.data_ptr(),
+                     ctypes.c_float(1e-6), ctypes.c_float(1e6), ctypes.c_float(1.0),
+                     qox.data_ptr(), kcx.data_ptr(), vcx.data_ptr(), stream)
+            ms = timed(torch, [lambda: pa.lib.pa_attention_prologue(*pargs)], 200, 20)
+            moved = 2 * T * (Hq + 2 * Hkv) * D * 2
+            extra[f"prologue_T{T}"] = {
+                "description": f"QK-norm + NeoX RoPE + KV write of {T} tokens, Hq 40, Hkv 8, D 128",
+                "us_per_call": round(ms * 1e3, 2),
+                "bytes_moved_per_call": moved,
+                "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+            }
+            print(f"[bench] prologue T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+            del qx, kx, vx, kcx, vcx, qox
         result["other_workloads"] = extra
 
     if args.calibrate_copy:

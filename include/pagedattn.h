@@ -1,6 +1,8 @@
 /*
  * pagedattn.h -- C ABI of libpagedattn: single-token (decode) GQA attention over
- * a paged BF16 K/V cache, for AMD Instinct MI355X (gfx950).
+ * a paged BF16 K/V cache, for AMD Instinct MI355X (gfx950), with the steps
+ * around it: the paged KV write, FP8 pools, causal multi-query attention
+ * (chunked prefill, multi-token decode) and the QK-norm/RoPE/KV-write prologue.
  *
  * What the library computes
  *   For every sequence b and query head hq, with G = num_q_heads / num_kv_heads
@@ -260,6 +262,49 @@ pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const voi
                             const int32_t* context_lens, const int32_t* query_start,
                             float scale, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* ---- attention prologue: QK-norm, NeoX RoPE, KV write ----------------------
+ * The steps between the QKV projection and attention, fused in one kernel
+ * ("Qwen 3" TensorSharp docs, section 3 "Forward graph" and section 4.1
+ * "Attention"; "Qwen3-14B" pypto-lib page, "decode_fwd": Q/K norm -> RoPE ->
+ * KV cache write as the attention kernel's phase 0). For token t at position
+ * p = positions[t] and every head vector x of q and k (weight w = the q or k
+ * norm weight):
+ *   y = x / sqrt(mean(x^2) + eps) * w                        (per-head RMSNorm)
+ *   theta_i = p * rope_base^(-2i/D) / rope_scale,  i < D/2
+ *   out_i = y_i cos theta_i - y_{i+D/2} sin theta_i            (NeoX halves)
+ *   out_{i+D/2} = y_{i+D/2} cos theta_i + y_i sin theta_i
+ * q's result goes to q_out (not yet multiplied by the logit scale, which the
+ * attention call applies); k's result and v (unchanged) go to slot
+ * slot_mapping[t] of the pools, as pa_kv_write stores them. Angles are
+ * computed in FP64 per token, the rest in FP32; outputs round to nearest even. */
+typedef struct {
+  int32_t num_tokens;         /* T >= 0 (T == 0: nothing to do, PA_OK)          */
+  int32_t num_q_heads;        /* Hq >= 1, multiple of num_kv_heads              */
+  int32_t num_kv_heads;       /* Hkv >= 1                                       */
+  int32_t head_dim;           /* D in {128, 256}                                */
+  int32_t page_size;          /* P == 128                                       */
+  int32_t num_pages;          /* N >= 1: pages in each pool                     */
+} pa_prologue_shape_t;
+
+/* Enqueue the prologue on `stream`.
+ *   q            device, BF16 [T, Hq, D], 16-byte aligned (the projection's q)
+ *   k, v         device, BF16 [T, Hkv, D], 16-byte aligned
+ *   q_norm_weight, k_norm_weight   device, BF16 [D], 16-byte aligned
+ *   positions    device, INT32 [T]: each token's position (any value)
+ *   slot_mapping device, INT32 [T]: flat slot page * P + offset; negative
+ *                (padding) or >= N * P writes nothing to the pools
+ *   eps          finite, >= 0; rope_base, rope_scale finite, > 0
+ *   q_out        device, BF16 [T, Hq, D], 16-byte aligned; may equal q
+ *   k_cache,     device, BF16 [N, P, Hkv, D], 16-byte aligned, updated in place
+ *   v_cache
+ * Two tokens with the same slot: which one lands is unspecified. */
+pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* q, const void* k,
+                                  const void* v, const void* q_norm_weight,
+                                  const void* k_norm_weight, const int32_t* positions,
+                                  const int32_t* slot_mapping, float eps, float rope_base,
+                                  float rope_scale, void* q_out, void* k_cache, void* v_cache,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["decode_kernels.hip", "mq_kernels.hip", "kv_write.hip", "api.cpp"]
+SOURCES = ["decode_kernels.hip", "mq_kernels.hip", "kv_write.hip", "prologue.hip", "api.cpp"]
 HEADERS = ["launch.h", "device_common.h"]
 
 ARCH = "gfx950"

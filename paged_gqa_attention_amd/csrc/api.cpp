@@ -395,4 +395,54 @@ pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const voi
   return pa::launch_mq_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
+pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* q, const void* k,
+                                  const void* v, const void* q_norm_weight,
+                                  const void* k_norm_weight, const int32_t* positions,
+                                  const int32_t* slot_mapping, float eps, float rope_base,
+                                  float rope_scale, void* q_out, void* k_cache, void* v_cache,
+                                  void* stream) {
+  if (!shape) return PA_ERR_NULL_POINTER;
+  if (shape->num_tokens < 0 || shape->num_q_heads < 1 || shape->num_kv_heads < 1 ||
+      shape->head_dim < 1 || shape->page_size < 1 || shape->num_pages < 1)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (shape->num_q_heads % shape->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (shape->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+  if (shape->head_dim != 128 && shape->head_dim != 256) return PA_ERR_UNSUPPORTED;
+  // one workgroup per token; row offsets of q/out and of the pools fit size_t
+  if (shape->num_q_heads + 2 * shape->num_kv_heads > 1 << 16) return PA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !isfinite(eps) || !(rope_base > 0.0f) || !isfinite(rope_base) ||
+      !(rope_scale > 0.0f) || !isfinite(rope_scale))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (shape->num_tokens == 0) return PA_OK;
+  if (!q || !k || !v || !q_norm_weight || !k_norm_weight || !positions || !slot_mapping ||
+      !q_out || !k_cache || !v_cache)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_norm_weight) ||
+      !aligned16(k_norm_weight) || !aligned16(q_out) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || ((uintptr_t)positions & 3u) || ((uintptr_t)slot_mapping & 3u))
+    return PA_ERR_INVALID_ARGUMENT;
+  pa::PrologueArgs a;
+  a.q_in = static_cast<const uint16_t*>(q);
+  a.k_in = static_cast<const uint16_t*>(k);
+  a.v_in = static_cast<const uint16_t*>(v);
+  a.q_norm_w = static_cast<const uint16_t*>(q_norm_weight);
+  a.k_norm_w = static_cast<const uint16_t*>(k_norm_weight);
+  a.positions = positions;
+  a.slot_mapping = slot_mapping;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.num_tokens = shape->num_tokens;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.page_size = shape->page_size;
+  a.num_pages = shape->num_pages;
+  a.eps = eps;
+  a.rope_base = rope_base;
+  a.rope_scale = rope_scale;
+  a.stream = stream;
+  return pa::launch_prologue(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -79,4 +79,24 @@ int mq_row_tiles(int rows_per_head, int head_dim);
 int launch_mq(const MqLaunchArgs& a);
 int launch_mq_reduce(const MqLaunchArgs& a);
 
+// Arguments of the attention prologue (QK-norm, RoPE, KV write), validated.
+struct PrologueArgs {
+  const uint16_t* q_in;        // bf16 [T, Hq, D]
+  const uint16_t* k_in;        // bf16 [T, Hkv, D]
+  const uint16_t* v_in;        // bf16 [T, Hkv, D]
+  const uint16_t* q_norm_w;    // bf16 [D]
+  const uint16_t* k_norm_w;    // bf16 [D]
+  const int32_t* positions;    // int32 [T]
+  const int32_t* slot_mapping; // int32 [T]
+  uint16_t* q_out;             // bf16 [T, Hq, D] (may equal q_in)
+  uint16_t* k_cache;           // bf16 [N, P, Hkv, D]
+  uint16_t* v_cache;           // bf16 [N, P, Hkv, D]
+  int num_tokens, num_q_heads, num_kv_heads, head_dim, page_size, num_pages;
+  float eps, rope_base, rope_scale;
+  void* stream;                // hipStream_t
+};
+
+// Enqueue the prologue kernel; 0 on success, else the HIP error code.
+int launch_prologue(const PrologueArgs& a);
+
 }  // namespace pa

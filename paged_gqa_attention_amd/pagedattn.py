@@ -8,8 +8,8 @@ the library is missing, importing the binding raises instead of falling back.
 
 Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_plan``,
 ``pa_workspace_size``, ``pa_decode_partials``, ``pa_merge_partials``,
-``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_status_string``,
-``pa_abi_version``.
+``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_attention_prologue``,
+``pa_status_string``, ``pa_abi_version``.
 """
 
 from __future__ import annotations
@@ -79,6 +79,17 @@ class PaMqShape(ctypes.Structure):
     ]
 
 
+class PaPrologueShape(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+    ]
+
+
 class PagedAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -134,6 +145,13 @@ def _load():
         ctypes.POINTER(PaMqShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    lib.pa_attention_prologue.restype = ctypes.c_int
+    lib.pa_attention_prologue.argtypes = [
+        ctypes.POINTER(PaPrologueShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p,
     ]
     return lib
 
@@ -420,3 +438,53 @@ def pa_mq_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     if st != PA_OK:
         raise PagedAttnError(st, "pa_mq_attention")
     return out
+
+
+def pa_attention_prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                          positions: torch.Tensor, slot_mapping: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor, eps: float = 1e-6,
+                          rope_base: float = 1e6, rope_scale: float = 1.0,
+                          q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """QK-norm + NeoX RoPE + KV write of T new tokens; returns q_out [T, Hq, D].
+
+    q [T, Hq, D], k and v [T, Hkv, D], weights [D] (all bf16), positions and
+    slot_mapping [T] int32; k_cache / v_cache [N, 128, Hkv, D] bf16 are
+    updated in place (K after norm and RoPE, V as given).
+    """
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k_cache.dim() != 4 \
+            or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [T,Hq,D], k == v shape [T,Hkv,D], caches [N,P,Hkv,D]")
+    T, Hq, D = q.shape
+    if k.shape[0] != T or k.shape[2] != D or k_cache.shape[2:] != k.shape[1:]:
+        raise ValueError("q, k/v and the caches disagree on T, Hkv or D")
+    if q_norm_weight.shape != (D,) or k_norm_weight.shape != (D,):
+        raise ValueError("norm weights must be [D]")
+    if positions.shape != (T,) or slot_mapping.shape != (T,):
+        raise ValueError("positions and slot_mapping must be [T]")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("q_norm_weight", q_norm_weight, torch.bfloat16),
+                        ("k_norm_weight", k_norm_weight, torch.bfloat16),
+                        ("positions", positions, torch.int32),
+                        ("slot_mapping", slot_mapping, torch.int32),
+                        ("k_cache", k_cache, torch.bfloat16), ("v_cache", v_cache, torch.bfloat16)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU of q")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _check_out(q_out, q)
+    shape = PaPrologueShape(int(T), int(Hq), int(k.shape[1]), int(D), int(k_cache.shape[1]),
+                            int(k_cache.shape[0]))
+    st = _lib.pa_attention_prologue(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+                                    positions.data_ptr(), slot_mapping.data_ptr(),
+                                    ctypes.c_float(eps), ctypes.c_float(rope_base),
+                                    ctypes.c_float(rope_scale), q_out.data_ptr(),
+                                    k_cache.data_ptr(), v_cache.data_ptr(), _stream(q.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_attention_prologue")
+    return q_out

@@ -33,9 +33,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert names == ["pa_abi_version", "pa_decode", "pa_decode_fp8", "pa_decode_partials",
-                     "pa_kv_write", "pa_merge_partials", "pa_mq_attention", "pa_mq_plan",
-                     "pa_plan", "pa_status_string", "pa_workspace_size"]
+    assert names == ["pa_abi_version", "pa_attention_prologue", "pa_decode", "pa_decode_fp8",
+                     "pa_decode_partials", "pa_kv_write", "pa_merge_partials", "pa_mq_attention",
+                     "pa_mq_plan", "pa_plan", "pa_status_string", "pa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -287,3 +287,40 @@ def test_mq_rejects_bad_pointers():
     a = list(ok)
     a[9] = plan.workspace_bytes - 1
     assert pa.lib.pa_mq_attention(ctypes.byref(s), *a) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+
+
+# ---- attention prologue ----------------------------------------------------------
+
+def test_prologue_shape_struct():
+    assert ctypes.sizeof(pa.PaPrologueShape) == 6 * 4
+
+
+@fake_pointers
+def test_prologue_rejects_bad_arguments():
+    d = 1 << 20
+    good = lambda: pa.PaPrologueShape(16, 40, 8, 128, 128, 512)
+    ok = [d] * 7 + [ctypes.c_float(1e-6), ctypes.c_float(1e6), ctypes.c_float(1.0), d, d, d, None]
+    call = lambda s, a: pa.lib.pa_attention_prologue(ctypes.byref(s) if s is not None else None, *a)
+    assert call(None, ok) == pa.PA_ERR_NULL_POINTER
+    for field, value, code in (("num_tokens", -1, 2), ("num_q_heads", 0, 2), ("num_kv_heads", 3, 2),
+                               ("head_dim", 64, 3), ("page_size", 64, 3), ("num_pages", 0, 2)):
+        s = good()
+        setattr(s, field, value)
+        assert call(s, ok) == code, field
+    for i in (0, 1, 2, 3, 4, 5, 6, 10, 11, 12):
+        a = list(ok)
+        a[i] = None
+        assert call(good(), a) == pa.PA_ERR_NULL_POINTER, i
+    for i, bad in ((0, d + 2), (1, d + 8), (2, d + 4), (3, d + 2), (4, d + 8), (5, d + 2),
+                   (6, d + 1), (10, d + 8), (11, d + 2), (12, d + 4)):
+        a = list(ok)
+        a[i] = bad
+        assert call(good(), a) == pa.PA_ERR_INVALID_ARGUMENT, i
+    for i, val in ((7, -1.0), (7, float("nan")), (8, 0.0), (8, float("inf")), (9, -2.0),
+                   (9, float("nan"))):
+        a = list(ok)
+        a[i] = ctypes.c_float(val)
+        assert call(good(), a) == pa.PA_ERR_INVALID_ARGUMENT, (i, val)
+    s = good()
+    s.num_tokens = 0
+    assert call(s, [None] * 7 + ok[7:10] + [None, None, None, None]) == pa.PA_OK
