@@ -366,6 +366,13 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
   const int row = blockIdx.x * RPW + (int)threadIdx.x / TPR;
   if (row >= rows) return;
   const int d4 = ((int)threadIdx.x % TPR) * 4;
+  const float* ml = ws_ml + (size_t)row * num_splits * 2;
+  const float* acc = ws_acc + (size_t)row * num_splits * D + d4;
+  // The first chunk of partials loads together with the context length (one
+  // round trip, not two); splits past the context are loaded but not used.
+  float2 mlv[kMergeChunk];
+  f32x4 av[kMergeChunk];
+  merge_load<D>(ml, acc, 0, num_splits, mlv, av);
   const int ctx = context_lens[row / num_q_heads];
   f32x4 res;
   if (ctx < 0 || ctx > max_ctx) {
@@ -373,7 +380,13 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
     res = f32x4{nan, nan, nan, nan};
   } else {
     const int nv = (ctx + split_tokens - 1) / split_tokens;  // splits holding tokens
-    res = merge_row<D>(ws_acc, ws_ml, (size_t)row, num_splits, nv, d4);
+    MergeState st;
+    merge_fold(st, mlv, av, nv);
+    for (int s0 = kMergeChunk; s0 < nv; s0 += kMergeChunk) {
+      merge_load<D>(ml, acc, s0, nv - s0, mlv, av);
+      merge_fold(st, mlv, av, nv - s0);
+    }
+    res = merge_result(st, nv);
   }
   store_bf16x4(out + (size_t)row * D + d4, res);
 }

@@ -66,19 +66,29 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // consumed item's loads complete; the tail (< 2*NB-1 items) guards each one.
 // `load(item, slot)` and `use(item, slot)` receive compile-time slot indices
 // after unrolling.
+//
+// On the path into the steady-state loop the first NB-1 loads are issued
+// unconditionally: if some path could enter the loop with fewer loads in
+// flight, the compiler would have to assume the youngest loads are the ones
+// being used and wait for all of them, collapsing the pipeline to depth 1.
 template <int NB, class Load, class Use>
 __device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
-#pragma unroll
-  for (int i = 0; i < NB - 1; ++i)
-    if (i < n) load(i, i);
   int j = 0;
-  for (; j + 2 * NB - 2 < n; j += NB) {
+  if (n > 2 * NB - 2) {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      load(j + u + NB - 1, (u + NB - 1) % NB);
-      __builtin_amdgcn_sched_barrier(0);
-      use(j + u, u);
+    for (int i = 0; i < NB - 1; ++i) load(i, i);
+    for (; j + 2 * NB - 2 < n; j += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        load(j + u + NB - 1, (u + NB - 1) % NB);
+        __builtin_amdgcn_sched_barrier(0);
+        use(j + u, u);
+      }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i)
+      if (i < n) load(i, i);
   }
 #pragma unroll
   for (int u = 0; u < 2 * NB - 2; ++u) {
@@ -96,48 +106,70 @@ __device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
 // trip for the usual split counts. nv == 0 (empty context) gives zeros.
 constexpr int kMergeChunk = 8;
 
+struct MergeState {
+  float m = -INFINITY;  // running max of the folded m_s
+  float den = 0.f;      // sum 2^(m_s - m) l_s
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};  // sum 2^(m_s - m) acc_s
+};
+
+// Fold the first `count` (<= kMergeChunk) loaded partials into the state.
+__device__ __forceinline__ void merge_fold(MergeState& st, const float2 (&mlv)[kMergeChunk],
+                                           const f32x4 (&av)[kMergeChunk], int count) {
+  float mc = st.m;
+#pragma unroll
+  for (int i = 0; i < kMergeChunk; ++i)
+    if (i < count) mc = fmaxf(mc, mlv[i].x);
+  const float a = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mc);
+  st.den *= a;
+  st.num *= a;
+#pragma unroll
+  for (int i = 0; i < kMergeChunk; ++i) {
+    if (i < count) {
+      const float w = fast_exp2(mlv[i].x - mc);
+      st.den = fmaf(w, mlv[i].y, st.den);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.num[e] = fmaf(w, av[i][e], st.num[e]);
+    }
+  }
+  st.m = mc;
+}
+
+// Load the partials of splits s0 .. s0 + min(count, kMergeChunk) - 1.
+template <int D>
+__device__ __forceinline__ void merge_load(const float* ml, const float* acc, int s0, int count,
+                                           float2 (&mlv)[kMergeChunk], f32x4 (&av)[kMergeChunk]) {
+#pragma unroll
+  for (int i = 0; i < kMergeChunk; ++i) {
+    if (i < count) {
+      mlv[i] = *reinterpret_cast<const float2*>(ml + 2 * (s0 + i));
+      av[i] = *reinterpret_cast<const f32x4*>(acc + (size_t)(s0 + i) * D);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 merge_result(const MergeState& st, int nv) {
+  f32x4 res = {0.f, 0.f, 0.f, 0.f};
+  if (nv > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = st.num[e] / st.den;
+  }
+  return res;
+}
+
 template <int D>
 __device__ __forceinline__ f32x4 merge_row(const float* __restrict__ ws_acc,
                                            const float* __restrict__ ws_ml, size_t row,
                                            int num_splits, int nv, int d4) {
   const float* ml = ws_ml + row * num_splits * 2;
   const float* acc = ws_acc + row * num_splits * D + d4;
-  float m_run = -INFINITY, den = 0.f;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  MergeState st;
   for (int s0 = 0; s0 < nv; s0 += kMergeChunk) {
     float2 mlv[kMergeChunk];
     f32x4 av[kMergeChunk];
-#pragma unroll
-    for (int i = 0; i < kMergeChunk; ++i) {
-      if (s0 + i < nv) {
-        mlv[i] = *reinterpret_cast<const float2*>(ml + 2 * (s0 + i));
-        av[i] = *reinterpret_cast<const f32x4*>(acc + (size_t)(s0 + i) * D);
-      }
-    }
-    float mc = m_run;
-#pragma unroll
-    for (int i = 0; i < kMergeChunk; ++i)
-      if (s0 + i < nv) mc = fmaxf(mc, mlv[i].x);
-    const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mc);
-    den *= a;
-    num *= a;
-#pragma unroll
-    for (int i = 0; i < kMergeChunk; ++i) {
-      if (s0 + i < nv) {
-        const float w = fast_exp2(mlv[i].x - mc);
-        den = fmaf(w, mlv[i].y, den);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) num[e] = fmaf(w, av[i][e], num[e]);
-      }
-    }
-    m_run = mc;
+    merge_load<D>(ml, acc, s0, nv - s0, mlv, av);
+    merge_fold(st, mlv, av, nv - s0);
   }
-  f32x4 res = {0.f, 0.f, 0.f, 0.f};
-  if (nv > 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) res[e] = num[e] / den;
-  }
-  return res;
+  return merge_result(st, nv);
 }
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 v) {
