@@ -118,6 +118,7 @@ pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
     pps = (int)((w + splits_wanted - 1) / splits_wanted);
   }
   if (pps > w) pps = w;
+  if (pps > pa::kMqMaxSplitPages) pps = pa::kMqMaxSplitPages;  // page ids staged in LDS
   if (pps < 1) pps = 1;
   const int splits = (w + pps - 1) / pps;
   if (base * splits > INT32_MAX) return PA_ERR_UNSUPPORTED;

@@ -71,6 +71,9 @@ struct MqLaunchArgs {
   void* stream;                // hipStream_t
 };
 
+// Most pages one multi-query workgroup covers: their ids are staged in LDS.
+constexpr int kMqMaxSplitPages = 256;
+
 // Row tiles per workgroup for a given number of rows per (sequence, KV head).
 int mq_row_tiles(int rows_per_head, int head_dim);
 

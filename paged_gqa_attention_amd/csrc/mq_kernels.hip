@@ -74,10 +74,13 @@ __host__ __device__ constexpr int mq_nbuf(int rt) { return rt >= 4 ? 2 : 1; }
 __host__ __device__ constexpr int mq_prefetch(int d, int rt) { return rt >= 4 && d == 128 ? 2 : 1; }
 
 // LDS bytes: per stage, the K tiles of the KS streams, then their V tiles,
-// each tile 32 token rows of 2*D bytes. The end-of-kernel stream merge reuses
-// the space.
-__host__ __device__ constexpr int mq_lds_bytes(int d, int rt) {
+// each tile 32 token rows of 2*D bytes (the end-of-kernel stream merge reuses
+// this space); then the page ids of the workgroup's pages.
+__host__ __device__ constexpr int mq_stage_bytes(int d, int rt) {
   return mq_nbuf(rt) * 2 * mq_streams(d, rt) * kChunk * 2 * d;
+}
+__host__ __device__ constexpr int mq_lds_bytes(int d, int rt) {
+  return mq_stage_bytes(d, rt) + 4 * kMqMaxSplitPages;
 }
 
 // 16-byte chunk c of token row r of a tile is stored at chunk position
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
   static_assert(UPT * NT == 2 * KS * kChunk * CPR, "staging must tile evenly");
   static_assert(UPT % 2 == 0, "half K, half V");
   static_assert(KS == 1 || TPW == 1, "the stream merge handles one row tile per wave");
-  static_assert(mq_lds_bytes(D, RT) == NBUF * STAGE, "LDS size");
+  static_assert(mq_stage_bytes(D, RT) == NBUF * STAGE, "LDS size");
 
   extern __shared__ __attribute__((aligned(16))) char smem_mq[];
   lds_char* lds = (lds_char*)smem_mq;
@@ -245,13 +248,26 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
 
   u32x4 stg[PF][UPT];
   bool stg_bad[PF];
-  int next_page = n_it > 0 ? bt_row[t_begin / kMqPage] : 0;
+
+  // The page ids of the workgroup's range (at most kMqMaxSplitPages, the
+  // plan's cap) go to LDS once. Each iteration's id is read from there one
+  // issue ahead: an LDS read completes in order with the staging stores, so
+  // the wait for it never covers later work (a scalar load would make every
+  // wait on the LDS counter a full drain).
+  int* s_pages = reinterpret_cast<int*>(smem_mq + mq_stage_bytes(D, RT));
+  {
+    const int first_pg = t_begin / kMqPage;
+    const int npg = n_it > 0 ? (t_end - 1) / kMqPage - first_pg + 1 : 0;
+    for (int i = tid; i < npg; i += NT) s_pages[i] = bt_row[first_pg + i];
+    __syncthreads();
+  }
+  int next_page = n_it > 0 ? s_pages[0] : 0;  // same value in every lane
 
   // Loads of iteration it (called in increasing it) into register slot `slot`.
   auto issue = [&](int it, int slot) {
     const int tb = t_begin + it * IT;
-    const int page = next_page;
-    if (it + 1 < n_it) next_page = bt_row[(tb + IT) / kMqPage];
+    const int page = __builtin_amdgcn_readfirstlane(next_page);
+    if (it + 1 < n_it) next_page = s_pages[(tb + IT - t_begin) / kMqPage];
     stg_bad[slot] = (unsigned)page >= (unsigned)num_pages;
     const size_t base = (size_t)(stg_bad[slot] ? 0 : page) * page_elems + (size_t)h * D +
                         (size_t)(tb & (kMqPage - 1)) * row_elems;
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
       // the exact row max across lanes and rescale (a wave-uniform branch).
       // Every term and the sum use the same reference: the result is the
       // same softmax.
-      if (__builtin_amdgcn_ballot_w64(lmax > m_run[tt] + kRescale)) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(lmax > m_run[tt] + kRescale) != 0, 0)) {
         float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_ref = mx > m_run[tt] + kRescale ? mx : m_run[tt];  // same on the row
