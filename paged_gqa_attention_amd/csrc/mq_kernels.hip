@@ -511,6 +511,276 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
   }
 }
 
+// 128 rows per workgroup for head_dim 128, as 4 waves of 32 rows on
+// v_mfma_f32_32x32x16_bf16: every K and V^T operand read from LDS feeds 32
+// rows (twice what the 16-row tiles get), halving LDS traffic per flop.
+// Output element i of lane l of this MFMA is D[8*(i/4) + 4*(l/32) + i%4]
+// [l%32] (pinned on MI355X with an in-bounds probe), so with S^T = K . Q^T a
+// lane holds 16 scores of row l%32; its first and last 8 are the B operands of
+// the two 16-token P.V MFMAs (k index 8*(l/32) + j <-> the token of its
+// score), and the A operands (V^T) come from transposing LDS reads of rows
+// 16h + 4*(l/32) (+8). Staging, masking, lazy rescaling and the output
+// format are those of mq_kernel.
+constexpr int kM32Threads = 256;
+constexpr int kM32Rows = 128;
+__host__ __device__ constexpr int mq32_stage_bytes() { return 2 * 2 * kChunk * 2 * 128; }
+__host__ __device__ constexpr int mq32_lds_bytes() {
+  return mq32_stage_bytes() + 4 * kMqMaxSplitPages;
+}
+
+__global__ __launch_bounds__(kM32Threads) void mq32_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
+    uint16_t* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int batch, int num_tokens, int num_kv_heads, int gqa, int max_pages, int num_pages,
+    int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale) {
+  constexpr int D = 128;
+  constexpr int NT = kM32Threads;
+  constexpr int KD = D / 16;                // k-steps of the 32x32x16 score MFMA
+  constexpr int DB = D / 32;                // 32-dim output blocks
+  constexpr int CPR = D / 8;                // 16-byte chunks per token row
+  constexpr int TILE = kChunk * 2 * D;      // bytes of one 32-token tile
+  constexpr int STAGE = 2 * TILE;           // K tile, then V tile
+  constexpr int UPT = 2 * kChunk * CPR / NT;
+  constexpr int IT = kChunk;
+  constexpr int PF = 2;
+  static_assert(UPT * NT == 2 * kChunk * CPR && UPT % 2 == 0, "staging");
+  static_assert(2 * STAGE == mq32_stage_bytes(), "LDS size");
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+  extern __shared__ __attribute__((aligned(16))) char smem_mq[];
+  lds_char* lds = (lds_char*)smem_mq;
+
+  const int num_pairs = batch * num_kv_heads;
+  const int pair = blockIdx.x % num_pairs;
+  const int rest = blockIdx.x / num_pairs;
+  const int rb = row_blocks - 1 - rest % row_blocks;  // longest row blocks first
+  const int s = rest / row_blocks;
+  const int h = pair % num_kv_heads;
+  const int b = pair / num_kv_heads;
+  const int num_q_heads = num_kv_heads * gqa;
+
+  const int qs0 = query_start[b];
+  const int lqn = query_start[b + 1] - qs0;
+  if (qs0 < 0 || lqn <= 0 || lqn > max_query_len || qs0 > num_tokens - lqn) return;
+  const int rows_b = lqn * gqa;
+  const int row0 = rb * kM32Rows;
+  if (row0 >= rows_b) return;
+  const int ctx = context_lens[b];
+  const bool bad_ctx = ctx < 0 || ctx > max_pages * kMqPage;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;    // token group of the lane in the 32x32 layouts
+  const int lr = lane & 31;   // the lane's row within the wave's 32
+
+  const int split_tokens = split_pages * kMqPage;
+  const int t_begin = s * split_tokens;
+  const int last_row = min(row0 + kM32Rows, rows_b) - 1;
+  const int n_last = bad_ctx ? 0 : ctx - lqn + last_row / gqa + 1;
+  const int t_end = min(t_begin + split_tokens, n_last);
+  if (num_splits > 1 && (bad_ctx || t_end <= t_begin)) return;
+
+  const int row = row0 + 32 * wave + lr;
+  const bool row_ok = row < rows_b;
+  const int i_tok = row_ok ? row / gqa : 0;
+  const int hq = h * gqa + (row_ok ? row - i_tok * gqa : 0);
+  const size_t orow = ((size_t)qs0 + i_tok) * num_q_heads + hq;
+  const int lim = row_ok ? min(ctx - lqn + i_tok + 1, t_end) : 0;
+  int lim_min = row_ok ? lim : INT32_MAX;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+
+  // B operand of the score MFMA, k-step kk: Q[row][16*kk + 8*g .. +7]
+  u32x4 qb[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk)
+    qb[kk] = row_ok ? load16(q + orow * D + 16 * kk + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+
+  const size_t page_elems = (size_t)kMqPage * num_kv_heads * D;
+  const size_t row_elems = (size_t)num_kv_heads * D;
+  const int32_t* bt_row = block_table + (size_t)b * max_pages;
+  const int n_it = t_end > t_begin ? (t_end - t_begin + IT - 1) / IT : 0;
+
+  u32x4 stg[PF][UPT];
+  bool stg_bad[PF];
+  int* s_pages = reinterpret_cast<int*>(smem_mq + mq32_stage_bytes());
+  {
+    const int first_pg = t_begin / kMqPage;
+    const int npg = n_it > 0 ? (t_end - 1) / kMqPage - first_pg + 1 : 0;
+    for (int i = tid; i < npg; i += NT) s_pages[i] = bt_row[first_pg + i];
+    __syncthreads();
+  }
+  int next_page = n_it > 0 ? s_pages[0] : 0;
+
+  auto issue = [&](int it, int slot) {
+    const int tb = t_begin + it * IT;
+    const int page = __builtin_amdgcn_readfirstlane(next_page);
+    if (it + 1 < n_it) next_page = s_pages[(tb + IT - t_begin) / kMqPage];
+    stg_bad[slot] = (unsigned)page >= (unsigned)num_pages;
+    const size_t base = (size_t)(stg_bad[slot] ? 0 : page) * page_elems + (size_t)h * D +
+                        (size_t)(tb & (kMqPage - 1)) * row_elems;
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = (tid + NT * k) % (NT * UPT / 2);
+      const uint16_t* pool = k < UPT / 2 ? k_cache : v_cache;
+      stg[slot][k] = load16(pool + base + (size_t)(u / CPR) * row_elems + 8 * (u % CPR));
+    }
+  };
+  auto commit = [&](int it, int slot) {
+    const int tb = t_begin + it * IT;
+    lds_char* stage = lds + (it & 1) * STAGE;
+    const bool plain = tb + IT <= t_end && !stg_bad[slot];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const bool is_k = k < UPT / 2;
+      const int u = (tid + NT * k) % (NT * UPT / 2);
+      const int c = u % CPR;
+      const int r = u / CPR;  // token row of the chunk
+      u32x4 v = stg[slot][k];
+      if (!plain) {
+        if (tb + r >= t_end) v = u32x4{0u, 0u, 0u, 0u};
+        else if (stg_bad[slot]) v = is_k ? u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}
+                                         : u32x4{0u, 0u, 0u, 0u};
+      }
+      const uint32_t off = is_k ? k_off<D>(r, c) : (uint32_t)TILE + v_off<D>(r, c);
+      *(u32x4 __attribute__((address_space(3)))*)(stage + off) = v;
+    }
+  };
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+
+  // V^T operand reads: 16-lane group q' = lane/16 covers dims 16*(q' & 1) of
+  // the 32-dim block; lane (4*jj + c4) of the group points at 4 dims of row
+  // rowbase + jj.
+  const int sub = (lane >> 4) & 1;
+  const int vjj = (lane & 15) >> 2;
+  const int vc4 = lane & 3;
+
+  auto compute = [&](int it) {
+    const lds_char* kt = lds + (it & 1) * STAGE;
+    const lds_char* vt = kt + TILE;
+    const int tb = t_begin + it * IT;
+    u32x4 ka[KD];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+      ka[kk] = *(const u32x4 __attribute__((address_space(3)))*)(kt + k_off<D>(lr, 2 * kk + g));
+    u32x4 va[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int cc = 4 * db + 2 * sub + (vc4 >> 1);
+        const uint32_t so = 8u * (vc4 & 1);
+        const u32x2 lo = lds_read_tr16(vt, v_off<D>(16 * hh + 4 * g + vjj, cc) + so);
+        const u32x2 hi = lds_read_tr16(vt, v_off<D>(16 * hh + 8 + 4 * g + vjj, cc) + so);
+        va[db][hh] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
+                                                     __builtin_bit_cast(bf16x8, qb[kk]), sacc, 0,
+                                                     0, 0);
+    // lane: sacc[i] = S[row lr][token tb + 8*(i/4) + 4*g + i%4]
+    const bool full = tb + kChunk <= lim_min;
+    float sc[16];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = sacc[i] * score_scale;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = tb + 8 * (i >> 2) + 4 * g + (i & 3);
+        sc[i] = t < lim ? sacc[i] * score_scale : -INFINITY;
+      }
+    }
+    float lmax = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, sc[i]);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(lmax > m_run + kRescale) != 0, 0)) {
+      const float mx = fmaxf(lmax, __shfl_xor(lmax, 32));
+      const float m_ref = mx > m_run + kRescale ? mx : m_run;  // same on both lanes of the row
+      const float alpha = m_ref == m_run ? 1.f : fast_exp2(m_run - m_ref);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_ref;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8 pb[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x8 p;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(sc[8 * hh + j] - m_use);
+      pb[hh] = __builtin_convertvector(p, bf16x8);
+      ps += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    l_run += ps;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[db][hh]),
+                                                        pb[hh], o[db], 0, 0, 0);
+  };
+
+  staged_loop<PF>(
+      n_it, [&](int it, int slot) { issue(it, slot); },
+      [&](int it, int slot, auto&& next) {
+        commit(it, slot);
+        next();
+        __syncthreads();
+        compute(it);
+      });
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  // lane holds dims 32*db + 8*qq + 4*g + (0..3), qq = 0..3, of its row
+  if (num_splits == 1) {
+    uint16_t* dst = out + orow * D + 4 * g;
+    if (bad_ctx) {
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          store_bf16x4(dst + 32 * db + 8 * qq, f32x4{nan, nan, nan, nan});
+    } else {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          store_bf16x4(dst + 32 * db + 8 * qq,
+                       f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2],
+                             o[db][4 * qq + 3]} * inv);
+    }
+  } else {
+    const size_t slot = orow * num_splits + s;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<f32x4*>(ws_acc + slot * D + 32 * db + 8 * qq + 4 * g) =
+            f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
+    if (g == 0) *reinterpret_cast<float2*>(ws_ml + slot * 2) = make_float2(m_run, l_tot);
+  }
+}
+
 // Merge of the splits of every (query token, query head) row: one thread per 4
 // dims. The row's sequence is found by binary search in query_start.
 template <int D>
@@ -566,13 +836,32 @@ int launch_mq_drt(const MqLaunchArgs& a) {
                               dim3(64 * mq_waves(D, RT)), args, mq_lds_bytes(D, RT), stream);
 }
 
+int launch_mq32(const MqLaunchArgs& a) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
+  const int gqa = a.num_q_heads / a.num_kv_heads;
+  const dim3 grid(a.batch * a.num_kv_heads * a.row_blocks * a.num_splits);
+  void* args[] = {(void*)&a.q,           (void*)&a.k_cache,       (void*)&a.v_cache,
+                  (void*)&a.block_table, (void*)&a.context_lens,  (void*)&a.query_start,
+                  (void*)&a.out,         (void*)&a.ws_acc,        (void*)&a.ws_ml,
+                  (void*)&a.batch,       (void*)&a.num_tokens,    (void*)&a.num_kv_heads,
+                  (void*)&gqa,           (void*)&a.max_pages,     (void*)&a.num_pages,
+                  (void*)&a.max_query_len, (void*)&a.row_blocks,  (void*)&a.split_pages,
+                  (void*)&a.num_splits,  (void*)&a.score_scale};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq32_kernel), grid,
+                              dim3(kM32Threads), args, mq32_lds_bytes(), stream);
+}
+
 template <int D>
 int launch_mq_d(const MqLaunchArgs& a) {
   switch (a.row_tiles) {
-    case 1: return D == 128 ? launch_mq_drt<128, 1>(a) : -1;
+    case 1:
+      if constexpr (D == 128) return launch_mq_drt<128, 1>(a);
+      else return -1;  // head_dim 256 plans start at 2 row tiles
     case 2: return launch_mq_drt<D, 2>(a);
     case 4: return launch_mq_drt<D, 4>(a);
-    default: return launch_mq_drt<D, 8>(a);
+    default:
+      if constexpr (D == 128) return launch_mq32(a);
+      else return launch_mq_drt<D, 8>(a);
   }
 }
 
