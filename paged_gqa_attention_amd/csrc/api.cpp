@@ -11,17 +11,15 @@
 namespace {
 
 // MI355X has 256 compute units. When every sequence is at its maximum length
-// the plan aims for two 4-wave workgroups per CU: long splits amortise each
-// workgroup's fixed start and end latency, and two per CU keep enough loads in
-// flight (measured on MI355X: 8-page splits beat 4-page splits at batch 16).
+// the decode plan aims for 2048 partition waves (two 4-wave workgroups per CU):
+// long splits amortise each wave's fixed start and end latency, and eight
+// waves per CU keep enough loads in flight.
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kTargetWorkgroups = 2 * kComputeUnits;
-// The automatic plan keeps a split's score tile within 32 KiB of LDS; an
-// explicit split_pages may use up to 64 KiB.
-constexpr size_t kAutoLdsScoreBytes = 32 * 1024;
-constexpr size_t kMaxLdsBytes = 64 * 1024;
-
-int head_pad(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
+constexpr int64_t kTargetWaves = 4 * kTargetWorkgroups;
+// A decode split's score tile (split tokens x padded heads, FP32) lives in the
+// LDS of its wave; it is kept within 16 KiB (64 KiB per 4-wave workgroup).
+constexpr size_t kMaxWaveLdsBytes = 16 * 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -34,8 +32,7 @@ pa_status_t check_shape(const pa_shape_t* s) {
   if (s->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
   const int g = s->num_q_heads / s->num_kv_heads;
   if (!pa::has_kernels(s->head_dim, g)) return PA_ERR_UNSUPPORTED;
-  // grid limits (batch and KV heads are grid dimensions) and 32-bit offsets
-  // inside one page / one block-table row
+  // grid limits and 32-bit offsets inside one page / one block-table row
   if (s->batch > 65535 || s->num_kv_heads > 4096 || s->max_pages_per_seq > (1 << 20))
     return PA_ERR_UNSUPPORTED;
   return PA_OK;
@@ -45,20 +42,17 @@ pa_status_t check_shape(const pa_shape_t* s) {
 int choose_split_pages(const pa_shape_t* s) {
   const int g = s->num_q_heads / s->num_kv_heads;
   const int w = s->max_pages_per_seq;
-  const size_t row_bytes = sizeof(float) * (size_t)head_pad(g) * PA_PAGE_SIZE;  // per page
   int pps;
   if (s->split_pages > 0) {
     pps = s->split_pages;
-    int cap = 1;
-    while (cap < w && pa::partition_lds_bytes(s->head_dim, g, cap + 1) <= kMaxLdsBytes) ++cap;
-    if (pps > cap) pps = cap;
   } else {
     const int64_t pairs = (int64_t)(s->batch > 0 ? s->batch : 1) * s->num_kv_heads;
-    const int64_t splits_wanted = (kTargetWorkgroups + pairs - 1) / pairs;
+    const int64_t splits_wanted = (kTargetWaves + pairs - 1) / pairs;
     pps = (int)((w + splits_wanted - 1) / splits_wanted);
-    const int cap = (int)(kAutoLdsScoreBytes / row_bytes);
-    if (pps > cap) pps = cap > 0 ? cap : 1;
   }
+  int cap = 1;  // largest split whose score tile fits one wave's LDS share
+  while (pa::partition_wave_lds_bytes(s->head_dim, g, cap + 1) <= kMaxWaveLdsBytes) ++cap;
+  if (pps > cap) pps = cap;
   if (pps > w) pps = w;
   if (pps < 1) pps = 1;
   return pps;
@@ -66,9 +60,14 @@ int choose_split_pages(const pa_shape_t* s) {
 
 pa_status_t make_plan(const pa_shape_t* s, pa_plan_t* p) {
   const int pps = choose_split_pages(s);
-  const int splits = (s->max_pages_per_seq + pps - 1) / pps;
-  // the partition kernel's 1-D grid has batch * num_kv_heads * splits workgroups
-  if ((int64_t)s->batch * s->num_kv_heads * splits > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  // a workgroup's waves cover heads_per_workgroup KV heads and the rest of its
+  // waves consecutive splits: the split count is rounded up to fill them (the
+  // extra splits start past every context and write nothing)
+  const int hpw = pa::heads_per_workgroup(s->num_kv_heads);
+  const int wph = 4 / hpw;
+  const int splits = ((s->max_pages_per_seq + pps - 1) / pps + wph - 1) / wph * wph;
+  if ((int64_t)s->batch * (s->num_kv_heads / hpw) * (splits / wph) > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
   const size_t rows = (size_t)s->batch * s->num_q_heads * splits;
   p->split_pages = pps;
   p->num_splits = splits;

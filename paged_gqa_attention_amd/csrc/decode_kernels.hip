@@ -9,19 +9,23 @@
 // table ("Qwen 3" TensorSharp docs, section 11).
 //
 // Work decomposition
-//   partition_kernel<D, G>: one workgroup (4 waves) per (split s, KV head h,
-//   sequence b). A split is `split_pages` consecutive pages of the sequence.
+//   partition_kernel<D, G>: one wave per (sequence b, KV head h, split s); a
+//   split is `split_pages` consecutive pages of the sequence. A 4-wave
+//   workgroup holds up to 4 adjacent KV heads of one sequence (and, with fewer
+//   KV heads, consecutive splits), so its loads cover several heads' bytes of
+//   every token row together (measured on MI355X: ~12% more bandwidth than one
+//   head per workgroup). Each wave works alone, with no workgroup barrier:
 //   1. q . K^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with the G query
 //      heads of the group as the 16 rows of A (zero padded) and 16 tokens as
 //      the columns of B. Each lane loads 64 contiguous bytes of one token row
 //      per MFMA k-step, so one load instruction covers 16 rows x 64 B.
 //      Scores are scaled by scale*log2(e) in FP32, tail slots are masked by
-//      select, and the [token][head] score tile goes to LDS.
+//      select, and the [token][head] score tile goes to the wave's LDS.
 //   2. Per head: max over the split, p = 2^(s - max), l = sum p (FP32, fixed
-//      order), all in LDS.
+//      order), in the wave's LDS.
 //   3. P.V on the vector ALUs in FP32: each load instruction reads whole token
 //      rows (16 lanes x 16 B for D=128), every lane accumulates G heads x 8
-//      dims, then rows and waves are summed in a fixed order.
+//      dims, then the rows are summed in a fixed order.
 //   The unnormalised output, the max and the sum of each split go to an FP32
 //   workspace.
 //   reduce_kernel<D>: merges, for every (sequence, query head), the splits that
@@ -48,6 +52,7 @@ constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
 constexpr int kKSlots = 2;      // register slots of the K pipeline
 constexpr int kVSlots = 2;      // register slots of the V pipeline
+constexpr int kReduceChunk = 16; // splits the merge kernel loads per round trip
 
 // Score row stride in LDS: G padded to a power of two >= 4, so that one
 // 16-byte store per MFMA lane group lands a whole group of 4 heads.
@@ -56,21 +61,11 @@ struct HeadPad {
   static constexpr int value = G <= 4 ? 4 : (G <= 8 ? 8 : 16);
 };
 
-// LDS of the partition kernel, in 4-byte words:
-//   [score tile: split_tokens x GP floats, reused as 2 x G x D partial sums]
-//   [cross-wave scratch: 2 x 4 waves x 16 floats]
-//   [page ids of the split: split_pages ints]
-template <int D, int G>
-__host__ __device__ constexpr int lds_tile_words(int split_pages) {
-  return split_pages * kPage * HeadPad<G>::value > 2 * G * D
-             ? split_pages * kPage * HeadPad<G>::value
-             : 2 * G * D;
-}
-constexpr int kRedWords = 2 * kWaves * 16;
-
-template <int D, int G>
-__host__ __device__ constexpr int lds_words(int split_pages) {
-  return lds_tile_words<D, G>(split_pages) + kRedWords + split_pages;
+// LDS of the partition kernel, in 4-byte words: every wave owns the score
+// tile of its split, split_tokens x GP floats.
+template <int G>
+__host__ __device__ constexpr int wave_tile_words(int split_pages) {
+  return split_pages * kPage * HeadPad<G>::value;
 }
 
 // kFp8: the K/V pools hold FP8 E4M3 codes (one byte per value) with
@@ -81,8 +76,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, int num_kv_heads, int max_pages, int num_pages,
-    int split_pages, int num_splits, float score_scale, float v_scale) {
+    float* __restrict__ ws_ml, int batch, int num_kv_heads, int heads_per_wg, int max_pages,
+    int num_pages, int split_pages, int num_splits, float score_scale, float v_scale) {
   static_assert(D == 128 || D == 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "gqa ratio");
   constexpr int ESZ = kFp8 ? 1 : 2;       // bytes per cached K/V value
@@ -100,34 +95,35 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 
   extern __shared__ float smem[];
 
-  // 1-D grid, (sequence, KV head) pair fastest: consecutive workgroups land on
-  // different XCDs (dispatch is round-robin over the 8 XCDs), so every XCD gets
-  // an even share of every split index, and the first split of every pair,
-  // which always holds tokens, is dispatched first.
-  const int num_pairs = gridDim.x / num_splits;
-  const int pair = blockIdx.x % num_pairs;
-  const int s = blockIdx.x / num_pairs;
-  const int h = pair % num_kv_heads;
-  const int b = pair / num_kv_heads;
-  const int num_q_heads = num_kv_heads * G;
-  const int split_tokens = split_pages * kPage;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane >> 4;  // MFMA lane group (0..3)
   const int lr = lane & 15;  // MFMA row / column inside the group
 
-  float* s_tile = smem;                                        // [tiles*16][GP]
-  float* red = smem + lds_tile_words<D, G>(split_pages);       // [2][4][16]
-  int* s_page = reinterpret_cast<int*>(red + kRedWords);       // [split_pages]
+  // 1-D grid; a workgroup covers heads_per_wg adjacent KV heads of one
+  // sequence and kWaves / heads_per_wg consecutive splits of it, one wave per
+  // (KV head, split): the workgroup's loads then cover heads_per_wg * D * ESZ
+  // contiguous bytes of every token row it reads. (Sequence, head group) units
+  // vary fastest, so consecutive workgroups land on different XCDs (dispatch
+  // is round-robin over the 8 XCDs) and the first splits go out first.
+  const int num_hg = num_kv_heads / heads_per_wg;
+  const int num_units = batch * num_hg;
+  const int unit = blockIdx.x % num_units;
+  const int sg = blockIdx.x / num_units;
+  const int b = unit / num_hg;
+  const int h = (unit - b * num_hg) * heads_per_wg + wave % heads_per_wg;
+  const int s = sg * (kWaves / heads_per_wg) + wave / heads_per_wg;
+  const int num_q_heads = num_kv_heads * G;
+  const int split_tokens = split_pages * kPage;
+  float* s_tile = smem + wave * wave_tile_words<G>(split_pages);  // [token][GP]
 
-  // The page ids of the split and q do not depend on the context length, so
-  // their loads go out together with it (one memory round trip, not three).
-  // Entries past the context are read but never used.
+  // The page ids of the split (lane i: page i), q and the context length load
+  // together (one memory round trip, not three). Entries past the context are
+  // read but never used.
   const int first_page = s * split_pages;
   int page_id = -1;
-  if ((int)threadIdx.x < split_pages && first_page + (int)threadIdx.x < max_pages)
-    page_id = block_table[(size_t)b * max_pages + first_page + threadIdx.x];
+  if (lane < split_pages && first_page + lane < max_pages)
+    page_id = block_table[(size_t)b * max_pages + first_page + lane];
   // A operand of the score MFMA: lane (lq, lr) holds 8 dims of q[head lr] per
   // k-step (zero rows for heads >= G), the same dims its K operand holds:
   // BF16 pools: k-step kk <-> dims 32*kk + 8*lq .. +7;
@@ -145,13 +141,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
   const int t0 = s * split_tokens;  // first token of this split
   const int n_s = min(ctx - t0, split_tokens);
-  if (n_s <= 0) return;  // split past the context: nothing to write
-
-  // Page ids this split needs; an id outside the pool becomes -1.
-  const int npg = (n_s + kPage - 1) / kPage;
-  if ((int)threadIdx.x < npg)
-    s_page[threadIdx.x] = (unsigned)page_id < (unsigned)num_pages ? page_id : -1;
-  __syncthreads();
+  if (n_s <= 0) return;  // split past the context: nothing to write (no barriers below)
+  page_id = (unsigned)page_id < (unsigned)num_pages ? page_id : -1;  // outside the pool: -1
 
   const size_t page_bytes = (size_t)kPage * num_kv_heads * D * ESZ;
   const uint32_t row_bytes = (uint32_t)num_kv_heads * D * ESZ;  // token stride
@@ -159,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 
   // Base of the page holding local token tl (wave-uniform); bad -> pool start.
   auto page_base = [&](const void* pool, int tl, bool& bad) -> const char* {
-    const int page = __builtin_amdgcn_readfirstlane(s_page[tl >> 7]);
+    const int page = __builtin_amdgcn_readlane(page_id, tl >> 7);
     bad = page < 0;
     return reinterpret_cast<const char*>(pool) + (size_t)(bad ? 0 : page) * page_bytes;
   };
@@ -170,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // row, so one load instruction covers 16 token rows x 64 contiguous bytes.
   // FP8 codes are widened to BF16 exactly before the MFMA.
   const uint32_t k_lane_off = (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
-  auto load_k = [&](int tile, u32x4 (&buf)[KL], bool& bad) {
+  auto load_k = [&](int tile, u32x4 (&buf)[KL], bool& bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
     const char* base = page_base(k_cache, tl, bad);
     const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + k_lane_off;
@@ -178,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     for (int j = 0; j < KL; ++j)
       buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
   };
-  auto score_tile = [&](int tile, const u32x4 (&buf)[KL], bool bad) {
+  auto score_tile = [&](int tile, const u32x4 (&buf)[KL], bool bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -205,13 +196,12 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   };
 
   const int ntile = (n_s + 15) >> 4;
-  const int nk = ntile > wave ? (ntile - 1 - wave) / kWaves + 1 : 0;  // tiles of this wave
   {
     u32x4 kbuf[KNB][KL];
     bool kbad[KNB];
     pipeline<KNB>(
-        nk, [&](int i, int slot) { load_k(wave + i * kWaves, kbuf[slot], kbad[slot]); },
-        [&](int i, int slot) { score_tile(wave + i * kWaves, kbuf[slot], kbad[slot]); });
+        ntile, [&](int i, int slot) __attribute__((always_inline)) { load_k(i, kbuf[slot], kbad[slot]); },
+        [&](int i, int slot) __attribute__((always_inline)) { score_tile(i, kbuf[slot], kbad[slot]); });
   }
 
   // ---- V loads of the first P.V step go out before the softmax ------------
@@ -220,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // one lane loads the 8 values of dims 8c .. 8c+7 (16 B of BF16, 8 B of FP8)
   using VChunk = typename std::conditional<kFp8, u32x2, u32x4>::type;
   const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 8u * ESZ * c;
-  auto load_v = [&](int blk, VChunk (&buf)[PV_U]) {
+  auto load_v = [&](int blk, VChunk (&buf)[PV_U]) __attribute__((always_inline)) {
     const int tl = blk * BR;
     bool bad;
     const char* base = page_base(v_cache, tl, bad);  // bad pages: scores are NaN already
@@ -230,41 +220,38 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
       buf[u] = *reinterpret_cast<const VChunk*>(base + off + (uint32_t)(u * RPI) * row_bytes);
   };
   const int nblk = (n_s + BR - 1) / BR;
-  const int nv = nblk > wave ? (nblk - 1 - wave) / kWaves + 1 : 0;  // blocks of this wave
   VChunk vbuf[VNB][PV_U];
 #pragma unroll
   for (int i = 0; i < VNB - 1; ++i)
-    if (i < nv) load_v(wave + i * kWaves, vbuf[i]);
-  __syncthreads();
+    if (i < nblk) load_v(i, vbuf[i]);
 
-  // ---- phase 2: softmax over the split, per head ------------------------
+  // The score tile is private to this wave: a wave's LDS accesses execute in
+  // program order, and the wavefront-scope fences keep the compiler from
+  // moving them across the phase boundaries.
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+  // ---- phase 2: softmax over the split, per head (wave-local) ------------
   {
     const int nval = ntile * 16 * GP;
-    const int col = threadIdx.x & (GP - 1);  // 256 % GP == 0: fixed column per thread
-    float mx = -INFINITY;
-    for (int e = threadIdx.x; e < nval; e += kThreads) mx = fmaxf(mx, s_tile[e]);
+    float mx = -INFINITY;  // lane's column (head) is lane % GP: 64 % GP == 0
+    for (int e = lane; e < nval; e += 64) mx = fmaxf(mx, s_tile[e]);
 #pragma unroll
     for (int off = GP; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane < GP) red[wave * 16 + lane] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[col], red[16 + col]), fmaxf(red[32 + col], red[48 + col]));
     float sum = 0.f;
-    for (int e = threadIdx.x; e < nval; e += kThreads) {
+    for (int e = lane; e < nval; e += 64) {
       const float p = fast_exp2(s_tile[e] - mx);
       s_tile[e] = p;
       sum += p;
     }
 #pragma unroll
     for (int off = GP; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
-    if (lane < GP) red[64 + wave * 16 + lane] = sum;
-    __syncthreads();
-    if ((int)threadIdx.x < G) {
-      const float l = (red[64 + col] + red[80 + col]) + (red[96 + col] + red[112 + col]);
-      float* ml = ws_ml + (((size_t)b * num_q_heads + (size_t)h * G + col) * num_splits + s) * 2;
+    if (lane < G) {
+      float* ml = ws_ml + (((size_t)b * num_q_heads + (size_t)h * G + lane) * num_splits + s) * 2;
       ml[0] = mx;
-      ml[1] = l;
+      ml[1] = sum;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
   // ---- phase 3: acc = P . V on the vector ALUs ----------------------------
   float acc[G][8];
@@ -273,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
 
-  auto pv_block = [&](int blk, VChunk (&buf)[PV_U]) {
+  auto pv_block = [&](int blk, VChunk (&buf)[PV_U]) __attribute__((always_inline)) {
     const int tl = blk * BR;
     if (tl + BR > n_s) {  // last block: rows past the context may hold NaN
 #pragma unroll
@@ -313,10 +300,10 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   };
   // the first VNB-1 blocks were issued before the softmax
   pipeline<VNB>(
-      nv, [&](int i, int slot) { if (i >= VNB - 1) load_v(wave + i * kWaves, vbuf[slot]); },
-      [&](int i, int slot) { pv_block(wave + i * kWaves, vbuf[slot]); });
+      nblk, [&](int i, int slot) __attribute__((always_inline)) { if (i >= VNB - 1) load_v(i, vbuf[slot]); },
+      [&](int i, int slot) __attribute__((always_inline)) { pv_block(i, vbuf[slot]); });
 
-  // rows -> one, inside the wave (lanes with the same chunk c)
+  // rows -> one, inside the wave (lanes with the same chunk c), fixed order
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
@@ -324,33 +311,17 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
 
-  // waves -> one, in LDS, fixed order: (w0 + w2) + (w1 + w3)
-  __syncthreads();  // every wave is done reading the probabilities
-  float* ra = smem;  // [2][G][D]
-  if (r == 0 && wave < 2) {
+  if (r == 0) {
+    float* dst = ws_acc + (((size_t)b * num_q_heads + (size_t)h * G) * num_splits + s) * D + 8 * c;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float* dst = &ra[(wave * G + g) * D + 8 * c];
-      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[g][0], acc[g][1], acc[g][2], acc[g][3]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[g][4], acc[g][5], acc[g][6], acc[g][7]};
+      const float sc = kFp8 ? v_scale : 1.f;
+      float* d = dst + (size_t)g * num_splits * D;
+      *reinterpret_cast<f32x4*>(d) =
+          f32x4{acc[g][0] * sc, acc[g][1] * sc, acc[g][2] * sc, acc[g][3] * sc};
+      *reinterpret_cast<f32x4*>(d + 4) =
+          f32x4{acc[g][4] * sc, acc[g][5] * sc, acc[g][6] * sc, acc[g][7] * sc};
     }
-  }
-  __syncthreads();
-  if (r == 0 && wave >= 2) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float* dst = &ra[((wave - 2) * G + g) * D + 8 * c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] += acc[g][e];
-    }
-  }
-  __syncthreads();
-  float* dst = ws_acc + (((size_t)b * num_q_heads + (size_t)h * G) * num_splits + s) * D;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D;
-    const int d = i - g * D;
-    const float sum = ra[i] + ra[G * D + i];
-    dst[(size_t)g * num_splits * D + d] = kFp8 ? sum * v_scale : sum;
   }
 }
 
@@ -370,9 +341,10 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
   const float* acc = ws_acc + (size_t)row * num_splits * D + d4;
   // The first chunk of partials loads together with the context length (one
   // round trip, not two); splits past the context are loaded but not used.
-  float2 mlv[kMergeChunk];
-  f32x4 av[kMergeChunk];
-  merge_load<D>(ml, acc, 0, num_splits, mlv, av);
+  constexpr int C = kReduceChunk;
+  float2 mlv[C];
+  f32x4 av[C];
+  merge_load<D, C>(ml, acc, 0, num_splits, mlv, av);
   const int ctx = context_lens[row / num_q_heads];
   f32x4 res;
   if (ctx < 0 || ctx > max_ctx) {
@@ -381,10 +353,10 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
   } else {
     const int nv = (ctx + split_tokens - 1) / split_tokens;  // splits holding tokens
     MergeState st;
-    merge_fold(st, mlv, av, nv);
-    for (int s0 = kMergeChunk; s0 < nv; s0 += kMergeChunk) {
-      merge_load<D>(ml, acc, s0, nv - s0, mlv, av);
-      merge_fold(st, mlv, av, nv - s0);
+    merge_fold<C>(st, mlv, av, nv);
+    for (int s0 = C; s0 < nv; s0 += C) {
+      merge_load<D, C>(ml, acc, s0, nv - s0, mlv, av);
+      merge_fold<C>(st, mlv, av, nv - s0);
     }
     res = merge_result(st, nv);
   }
@@ -394,13 +366,15 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
 template <int D, int G, bool kFp8>
 int launch_partition_dgt(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
-  const dim3 grid(a.num_splits * a.num_kv_heads * a.batch);
-  const size_t lds = sizeof(float) * lds_words<D, G>(a.split_pages);
+  const int hpw = heads_per_workgroup(a.num_kv_heads);
+  const dim3 grid(a.batch * (a.num_kv_heads / hpw) * (a.num_splits / (kWaves / hpw)));
+  const size_t lds = sizeof(float) * kWaves * wave_tile_words<G>(a.split_pages);
   void* args[] = {(void*)&a.q,           (void*)&a.k_cache,      (void*)&a.v_cache,
                   (void*)&a.block_table, (void*)&a.context_lens, (void*)&a.ws_acc,
-                  (void*)&a.ws_ml,       (void*)&a.num_kv_heads, (void*)&a.max_pages,
-                  (void*)&a.num_pages,   (void*)&a.split_pages,  (void*)&a.num_splits,
-                  (void*)&a.score_scale, (void*)&a.v_scale};
+                  (void*)&a.ws_ml,       (void*)&a.batch,        (void*)&a.num_kv_heads,
+                  (void*)&hpw,           (void*)&a.max_pages,    (void*)&a.num_pages,
+                  (void*)&a.split_pages, (void*)&a.num_splits,   (void*)&a.score_scale,
+                  (void*)&a.v_scale};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G, kFp8>),
                               grid, dim3(kThreads), args, lds, stream);
 }
@@ -437,19 +411,9 @@ typedef int (*LaunchFn)(const LaunchArgs&);
 const LaunchFn kPartition128[17] = PA_G_LIST(128);
 const LaunchFn kPartition256[17] = PA_G_LIST(256);
 
-template <int D>
-size_t lds_bytes_for(int g, int split_pages) {
-  switch (g) {
-#define PA_LDS_CASE(G) \
-  case G:              \
-    return sizeof(float) * lds_words<D, G>(split_pages);
-    PA_LDS_CASE(1) PA_LDS_CASE(2) PA_LDS_CASE(3) PA_LDS_CASE(4) PA_LDS_CASE(5) PA_LDS_CASE(6)
-    PA_LDS_CASE(7) PA_LDS_CASE(8) PA_LDS_CASE(9) PA_LDS_CASE(10) PA_LDS_CASE(11)
-    PA_LDS_CASE(12) PA_LDS_CASE(13) PA_LDS_CASE(14) PA_LDS_CASE(15) PA_LDS_CASE(16)
-#undef PA_LDS_CASE
-    default:
-      return 0;
-  }
+size_t wave_tile_bytes_for(int g, int split_pages) {
+  const int gp = g <= 4 ? 4 : (g <= 8 ? 8 : 16);
+  return sizeof(float) * (size_t)split_pages * kPage * gp;
 }
 
 }  // namespace
@@ -458,10 +422,13 @@ bool has_kernels(int head_dim, int gqa_ratio) {
   return (head_dim == 128 || head_dim == 256) && gqa_ratio >= 1 && gqa_ratio <= 16;
 }
 
-size_t partition_lds_bytes(int head_dim, int gqa_ratio, int split_pages) {
+int heads_per_workgroup(int num_kv_heads) {
+  return num_kv_heads % 4 == 0 ? 4 : (num_kv_heads % 2 == 0 ? 2 : 1);
+}
+
+size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_pages) {
   if (!has_kernels(head_dim, gqa_ratio)) return 0;
-  return head_dim == 128 ? lds_bytes_for<128>(gqa_ratio, split_pages)
-                         : lds_bytes_for<256>(gqa_ratio, split_pages);
+  return wave_tile_bytes_for(gqa_ratio, split_pages);
 }
 
 int launch_partition(const LaunchArgs& a) {

@@ -101,9 +101,9 @@ __device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
 
 // Log-sum-exp merge of the first nv split partials of one (sequence, query
 // head) row, for the 4 dims d4 .. d4+3: M = max m_s, out = sum 2^(m_s-M) acc_s
-// / sum 2^(m_s-M) l_s. The partials of up to kMergeChunk splits are loaded
-// together, then folded into a running state, so a row costs one memory round
-// trip for the usual split counts. nv == 0 (empty context) gives zeros.
+// / sum 2^(m_s-M) l_s. The partials of up to C splits are loaded together,
+// then folded into a running state, so a row costs one memory round trip per
+// C splits. nv == 0 (empty context) gives zeros.
 constexpr int kMergeChunk = 8;
 
 struct MergeState {
@@ -112,18 +112,19 @@ struct MergeState {
   f32x4 num = {0.f, 0.f, 0.f, 0.f};  // sum 2^(m_s - m) acc_s
 };
 
-// Fold the first `count` (<= kMergeChunk) loaded partials into the state.
-__device__ __forceinline__ void merge_fold(MergeState& st, const float2 (&mlv)[kMergeChunk],
-                                           const f32x4 (&av)[kMergeChunk], int count) {
+// Fold the first `count` (<= C) loaded partials into the state.
+template <int C>
+__device__ __forceinline__ void merge_fold(MergeState& st, const float2 (&mlv)[C],
+                                           const f32x4 (&av)[C], int count) {
   float mc = st.m;
 #pragma unroll
-  for (int i = 0; i < kMergeChunk; ++i)
+  for (int i = 0; i < C; ++i)
     if (i < count) mc = fmaxf(mc, mlv[i].x);
   const float a = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mc);
   st.den *= a;
   st.num *= a;
 #pragma unroll
-  for (int i = 0; i < kMergeChunk; ++i) {
+  for (int i = 0; i < C; ++i) {
     if (i < count) {
       const float w = fast_exp2(mlv[i].x - mc);
       st.den = fmaf(w, mlv[i].y, st.den);
@@ -134,12 +135,12 @@ __device__ __forceinline__ void merge_fold(MergeState& st, const float2 (&mlv)[k
   st.m = mc;
 }
 
-// Load the partials of splits s0 .. s0 + min(count, kMergeChunk) - 1.
-template <int D>
+// Load the partials of splits s0 .. s0 + min(count, C) - 1.
+template <int D, int C>
 __device__ __forceinline__ void merge_load(const float* ml, const float* acc, int s0, int count,
-                                           float2 (&mlv)[kMergeChunk], f32x4 (&av)[kMergeChunk]) {
+                                           float2 (&mlv)[C], f32x4 (&av)[C]) {
 #pragma unroll
-  for (int i = 0; i < kMergeChunk; ++i) {
+  for (int i = 0; i < C; ++i) {
     if (i < count) {
       mlv[i] = *reinterpret_cast<const float2*>(ml + 2 * (s0 + i));
       av[i] = *reinterpret_cast<const f32x4*>(acc + (size_t)(s0 + i) * D);
@@ -156,18 +157,18 @@ __device__ __forceinline__ f32x4 merge_result(const MergeState& st, int nv) {
   return res;
 }
 
-template <int D>
+template <int D, int C = kMergeChunk>
 __device__ __forceinline__ f32x4 merge_row(const float* __restrict__ ws_acc,
                                            const float* __restrict__ ws_ml, size_t row,
                                            int num_splits, int nv, int d4) {
   const float* ml = ws_ml + row * num_splits * 2;
   const float* acc = ws_acc + row * num_splits * D + d4;
   MergeState st;
-  for (int s0 = 0; s0 < nv; s0 += kMergeChunk) {
-    float2 mlv[kMergeChunk];
-    f32x4 av[kMergeChunk];
-    merge_load<D>(ml, acc, s0, nv - s0, mlv, av);
-    merge_fold(st, mlv, av, nv - s0);
+  for (int s0 = 0; s0 < nv; s0 += C) {
+    float2 mlv[C];
+    f32x4 av[C];
+    merge_load<D, C>(ml, acc, s0, nv - s0, mlv, av);
+    merge_fold<C>(st, mlv, av, nv - s0);
   }
   return merge_result(st, nv);
 }

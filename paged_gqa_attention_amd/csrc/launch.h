@@ -28,8 +28,14 @@ struct LaunchArgs {
 // True if a kernel pair is compiled for (head_dim, gqa_ratio).
 bool has_kernels(int head_dim, int gqa_ratio);
 
-// Bytes of dynamic LDS the partition kernel uses for one split.
-size_t partition_lds_bytes(int head_dim, int gqa_ratio, int split_pages);
+// Adjacent KV heads one partition workgroup (4 waves) covers: 4, 2 or 1. The
+// other kWaves / heads_per_workgroup waves take consecutive splits, so the
+// number of splits must be a multiple of 4 / heads_per_workgroup.
+int heads_per_workgroup(int num_kv_heads);
+
+// Bytes of LDS one partition wave uses for a split of split_pages pages (the
+// workgroup uses four times that); 0 if no kernel exists for the shape.
+size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_pages);
 
 // Enqueue the partition kernel (split partials -> workspace) or the reduce
 // kernel (workspace -> out). Return 0 on success, else the HIP error code of

@@ -68,9 +68,11 @@ def test_struct_layout_matches_header():
 
 @pytest.mark.parametrize("cfg,expect", [
     ((2, 40, 8, 128, 2, 4), (1, 2)),       # B=2, W=2: one page per split
-    ((16, 40, 8, 128, 32, 512), (8, 4)),   # 128 (seq, kv head) pairs -> 4 splits of 1024 tokens
-    ((256, 40, 8, 128, 32, 2050), (8, 4)), # one split wanted; 32 KiB score tile caps it at 8 pages
-    ((32, 16, 2, 256, 32, 1024), (4, 8)),  # 64 pairs -> 8 splits of 512 tokens
+    ((16, 40, 8, 128, 32, 512), (2, 16)),  # 128 (seq, kv head) pairs -> 16 waves of 256 tokens
+    ((256, 40, 8, 128, 32, 2050), (4, 8)), # one split wanted; 16 KiB wave score tile caps it at 4 pages
+    ((32, 16, 2, 256, 32, 1024), (1, 32)), # 64 pairs -> 32 splits of one page
+    ((3, 6, 2, 128, 5, 40), (1, 6)),       # 2 KV heads: 2 splits per workgroup, 5 splits -> 6
+    ((3, 3, 1, 128, 5, 40), (1, 8)),       # 1 KV head: 4 splits per workgroup, 5 splits -> 8
 ])
 def test_plan_for_the_standard_workloads(cfg, expect):
     plan = pa.pa_plan(pa.make_shape(*cfg))
@@ -83,15 +85,23 @@ def test_plan_for_the_standard_workloads(cfg, expect):
 
 
 def test_plan_explicit_split_pages_and_clamp():
-    for sp in (1, 2, 3, 7, 15):
+    for sp in (1, 2, 3, 4):
         plan = pa.pa_plan(pa.make_shape(4, 40, 8, 128, 32, 200, split_pages=sp))
         assert plan.split_pages == sp
         assert plan.num_splits == -(-32 // sp)
-    # a split whose score tile would exceed 64 KiB of LDS is clamped
-    plan = pa.pa_plan(pa.make_shape(4, 40, 8, 128, 32, 200, split_pages=32))
-    assert 1 <= plan.split_pages < 32
+    # a split whose score tile would exceed one wave's 16 KiB of LDS is
+    # clamped: G=5 pads to 8 heads, 4 KiB per page
+    for sp in (5, 7, 32):
+        plan = pa.pa_plan(pa.make_shape(4, 40, 8, 128, 32, 200, split_pages=sp))
+        assert (plan.split_pages, plan.num_splits) == (4, 8)
+    # G=1 pads to 4 heads: 8 pages; and never more than the table's width
+    plan = pa.pa_plan(pa.make_shape(4, 4, 4, 128, 32, 200, split_pages=9))
+    assert plan.split_pages == 8
     plan = pa.pa_plan(pa.make_shape(4, 4, 4, 128, 2, 20, split_pages=9))
     assert plan.split_pages == 2
+    # G=16 pads to 16 heads: 2 pages
+    plan = pa.pa_plan(pa.make_shape(4, 32, 2, 128, 32, 200, split_pages=9))
+    assert (plan.split_pages, plan.num_splits) == (2, 16)
 
 
 @fake_pointers

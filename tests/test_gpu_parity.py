@@ -53,11 +53,16 @@ def test_edge_context_lengths_with_poison():
     assert_parity(out, ref, "edge contexts")
 
 
-@pytest.mark.parametrize("split_pages", [1, 2, 3, 4, 5, 8, 15])
-def test_split_sizes(split_pages):
+# explicit splits up to each ratio's cap (a wave's score tile holds 4, 8 or 2
+# pages for padded head counts 4, 8 and 16); 2 KV heads put two splits in a
+# workgroup, 8 KV heads one
+@pytest.mark.parametrize("G,Hkv,split_pages", [(5, 8, 1), (5, 8, 2), (5, 8, 3), (5, 8, 4),
+                                               (1, 8, 5), (2, 8, 8), (4, 2, 7), (16, 2, 1),
+                                               (16, 2, 2), (8, 2, 3)])
+def test_split_sizes(G, Hkv, split_pages):
     ctx = [1, 129, 700, 2049, 4096, 3000]
-    announce(f"split_pages={split_pages}")
-    w = workloads.build(len(ctx), 40, 8, 128, ctx, seed=11, max_pages=32, pool="permutation")
+    announce(f"G={G} Hkv={Hkv} split_pages={split_pages}")
+    w = workloads.build(len(ctx), G * Hkv, Hkv, 128, ctx, seed=11, max_pages=32, pool="permutation")
     w = workloads.poison_unused(w)
     assert_parity(run_gpu(w, split_pages=split_pages), run_oracle(w), f"split {split_pages}")
 
