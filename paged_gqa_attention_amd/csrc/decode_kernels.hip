@@ -21,8 +21,9 @@
 //      per MFMA k-step, so one load instruction covers 16 rows x 64 B.
 //      Scores are scaled by scale*log2(e) in FP32, tail slots are masked by
 //      select, and the [token][head] score tile goes to the wave's LDS.
-//   2. Per head: max over the split, p = 2^(s - max), l = sum p (FP32, fixed
-//      order), in the wave's LDS.
+//   2. Per head: max over the split (from running maxima kept in phase 1),
+//      then p = 2^(s - max) and l = sum p in one pass over the wave's LDS tile
+//      (FP32).
 //   3. P.V on the vector ALUs in FP32: each load instruction reads whole token
 //      rows (16 lanes x 16 B for D=128), every lane accumulates G heads x 8
 //      dims, then the rows are summed in a fixed order.
@@ -53,6 +54,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kKSlots = 2;      // register slots of the K pipeline
 constexpr int kVSlots = 2;      // register slots of the V pipeline
 constexpr int kReduceChunk = 16; // splits the merge kernel loads per round trip
+constexpr int kReduceThreads = 256;  // threads per merge workgroup
 
 // Score row stride in LDS: G padded to a power of two >= 4, so that one
 // 16-byte store per MFMA lane group lands a whole group of 4 heads.
@@ -169,6 +171,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     for (int j = 0; j < KL; ++j)
       buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
   };
+  // running max of the scores this lane holds (heads 4*lq .. 4*lq+3)
+  float m_lane[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   auto score_tile = [&](int tile, const u32x4 (&buf)[KL], bool bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -189,8 +193,10 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
       const bool valid = tl + lr < n_s;
       f32x4 sv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
         sv[i] = bad ? __builtin_nanf("") : (valid ? acc[i] * score_scale : -INFINITY);
+        m_lane[i] = fmaxf(m_lane[i], sv[i]);
+      }
       *reinterpret_cast<f32x4*>(&s_tile[(tl + lr) * GP + 4 * lq]) = sv;
     }
   };
@@ -231,24 +237,55 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
   // ---- phase 2: softmax over the split, per head (wave-local) ------------
+  // The max comes from the running maxima of phase 1 (the 16 token lanes of
+  // each MFMA lane group reduced by shuffles). Then one pass over the tile in
+  // 16-byte LDS accesses, four per lane in flight: p = 2^(s - max), l = sum p.
+  // Lane L touches only the 4-head group L % (GP/4) of every token row.
   {
-    const int nval = ntile * 16 * GP;
-    float mx = -INFINITY;  // lane's column (head) is lane % GP: 64 % GP == 0
-    for (int e = lane; e < nval; e += 64) mx = fmaxf(mx, s_tile[e]);
+    constexpr int GP4 = GP / 4;  // 4-head groups per token row
 #pragma unroll
-    for (int off = GP; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    float sum = 0.f;
-    for (int e = lane; e < nval; e += 64) {
-      const float p = fast_exp2(s_tile[e] - mx);
-      s_tile[e] = p;
-      sum += p;
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m_lane[i] = fmaxf(m_lane[i], __shfl_xor(m_lane[i], off));
+    const int j = lane % GP4;  // this lane's head group (64 % GP4 == 0)
+    float mx[4], sum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mx[i] = __shfl(m_lane[i], 16 * j);
+      sum[i] = 0.f;
+    }
+    f32x4* tile4 = reinterpret_cast<f32x4*>(s_tile);
+    const int n4 = ntile * 16 * GP4;
+    for (int e0 = lane; e0 < n4; e0 += 4 * 64) {
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + 64 * u < n4) x[u] = tile4[e0 + 64 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (e0 + 64 * u < n4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[u][i] = fast_exp2(x[u][i] - mx[i]);
+            sum[i] += x[u][i];
+          }
+          tile4[e0 + 64 * u] = x[u];
+        }
+      }
     }
 #pragma unroll
-    for (int off = GP; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
-    if (lane < G) {
-      float* ml = ws_ml + (((size_t)b * num_q_heads + (size_t)h * G + lane) * num_splits + s) * 2;
-      ml[0] = mx;
-      ml[1] = sum;
+    for (int off = GP4; off < 64; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += __shfl_xor(sum[i], off);
+    if (lane < GP4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * lane + i;
+        if (g < G) {
+          float* ml = ws_ml + (((size_t)b * num_q_heads + (size_t)h * G + g) * num_splits + s) * 2;
+          *reinterpret_cast<float2*>(ml) = float2{mx[i], sum[i]};
+        }
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -325,15 +362,15 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   }
 }
 
-// Merge kernel: one 256-thread workgroup merges RPW (sequence, query head)
+// Merge kernel: one kReduceThreads-thread workgroup merges RPW (sequence, query head)
 // rows; each thread owns 4 consecutive dims of one row.
 template <int D>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out, int rows,
     int num_q_heads, int num_splits, int split_tokens, int max_ctx) {
   constexpr int TPR = D / 4;             // threads per row
-  constexpr int RPW = kThreads / TPR;    // rows per workgroup (8 or 4)
+  constexpr int RPW = kReduceThreads / TPR;  // rows per workgroup
   const int row = blockIdx.x * RPW + (int)threadIdx.x / TPR;
   if (row >= rows) return;
   const int d4 = ((int)threadIdx.x % TPR) * 4;
@@ -390,12 +427,12 @@ int launch_reduce_d(const LaunchArgs& a) {
   const int rows = a.batch * a.num_q_heads;
   const int split_tokens = a.split_pages * kPage;
   const int max_ctx = a.max_pages * kPage;
-  constexpr int RPW = kThreads / (D / 4);
+  constexpr int RPW = kReduceThreads / (D / 4);
   void* args[] = {(void*)&a.ws_acc,      (void*)&a.ws_ml,      (void*)&a.context_lens,
                   (void*)&a.out,         (void*)&rows,         (void*)&a.num_q_heads,
                   (void*)&a.num_splits,  (void*)&split_tokens, (void*)&max_ctx};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel<D>),
-                              dim3((rows + RPW - 1) / RPW), dim3(kThreads), args, 0, stream);
+                              dim3((rows + RPW - 1) / RPW), dim3(kReduceThreads), args, 0, stream);
 }
 
 typedef int (*LaunchFn)(const LaunchArgs&);
