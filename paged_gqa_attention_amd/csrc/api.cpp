@@ -64,7 +64,7 @@ pa_status_t make_plan(const pa_shape_t* s, pa_plan_t* p) {
   // waves consecutive splits: the split count is rounded up to fill them (the
   // extra splits start past every context and write nothing)
   const int hpw = pa::heads_per_workgroup(s->num_kv_heads);
-  const int wph = 4 / hpw;
+  const int wph = pa::splits_per_workgroup(s->num_kv_heads);
   const int splits = ((s->max_pages_per_seq + pps - 1) / pps + wph - 1) / wph * wph;
   if ((int64_t)s->batch * (s->num_kv_heads / hpw) * (splits / wph) > INT32_MAX)
     return PA_ERR_UNSUPPORTED;

@@ -49,12 +49,14 @@ namespace pa {
 namespace {
 
 constexpr int kPage = 128;      // tokens per page
-constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kThreads = 256;   // threads per partition workgroup (4 waves of 64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kKSlots = 2;      // register slots of the K pipeline
 constexpr int kVSlots = 2;      // register slots of the V pipeline
 constexpr int kReduceChunk = 16; // splits the merge kernel loads per round trip
 constexpr int kReduceThreads = 256;  // threads per merge workgroup
+// s_getreg operand for hwreg(HW_REG_HW_ID, 0, 4): the wave's slot on its SIMD
+constexpr int kHwIdWaveSlot = 4 | (0 << 6) | ((4 - 1) << 11);
 
 // Score row stride in LDS: G padded to a power of two >= 4, so that one
 // 16-byte store per MFMA lane group lands a whole group of 4 heads.
@@ -99,6 +101,17 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Two waves share each SIMD. Measured on MI355X, the older of the two runs
+  // ahead and the younger finishes alone, with fewer loads in flight per CU.
+  // The waves alternate their issue priority every 64 tokens (by the parity
+  // of their slot on the SIMD), which evens out their progress.
+  const int slot_parity = __builtin_amdgcn_s_getreg(kHwIdWaveSlot) & 1;
+  auto take_turn = [&](int token) __attribute__((always_inline)) {
+    if (((token >> 6) + slot_parity) & 1)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
   const int lq = lane >> 4;  // MFMA lane group (0..3)
   const int lr = lane & 15;  // MFMA row / column inside the group
 
@@ -165,6 +178,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const uint32_t k_lane_off = (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
   auto load_k = [&](int tile, u32x4 (&buf)[KL], bool& bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
+    take_turn(tl);
     const char* base = page_base(k_cache, tl, bad);
     const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + k_lane_off;
 #pragma unroll
@@ -218,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 8u * ESZ * c;
   auto load_v = [&](int blk, VChunk (&buf)[PV_U]) __attribute__((always_inline)) {
     const int tl = blk * BR;
+    take_turn(tl);
     bool bad;
     const char* base = page_base(v_cache, tl, bad);  // bad pages: scores are NaN already
     const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + v_lane_off;
@@ -460,8 +475,12 @@ bool has_kernels(int head_dim, int gqa_ratio) {
 }
 
 int heads_per_workgroup(int num_kv_heads) {
-  return num_kv_heads % 4 == 0 ? 4 : (num_kv_heads % 2 == 0 ? 2 : 1);
+  int hpw = kWaves;  // the largest power of two <= kWaves dividing num_kv_heads
+  while (num_kv_heads % hpw != 0) hpw /= 2;
+  return hpw;
 }
+
+int splits_per_workgroup(int num_kv_heads) { return kWaves / heads_per_workgroup(num_kv_heads); }
 
 size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_pages) {
   if (!has_kernels(head_dim, gqa_ratio)) return 0;

@@ -28,10 +28,12 @@ struct LaunchArgs {
 // True if a kernel pair is compiled for (head_dim, gqa_ratio).
 bool has_kernels(int head_dim, int gqa_ratio);
 
-// Adjacent KV heads one partition workgroup (4 waves) covers: 4, 2 or 1. The
-// other kWaves / heads_per_workgroup waves take consecutive splits, so the
-// number of splits must be a multiple of 4 / heads_per_workgroup.
+// Adjacent KV heads one partition workgroup covers (one wave per head and
+// split), and the consecutive splits it covers: their product is the number
+// of waves per workgroup, so the number of splits must be a multiple of
+// splits_per_workgroup.
 int heads_per_workgroup(int num_kv_heads);
+int splits_per_workgroup(int num_kv_heads);
 
 // Bytes of LDS one partition wave uses for a split of split_pages pages (the
 // workgroup uses four times that); 0 if no kernel exists for the shape.
