@@ -261,7 +261,7 @@ def main():
                         "128-token pages, 40 layers' 512-page pools called back to back",
             "batch": B, "context": int(w0.context_lens.max()), "num_q_heads": Hq,
             "num_kv_heads": Hkv, "head_dim": D, "page_size": P, "layers": L,
-            "split_pages": plan.split_pages, "num_splits": plan.num_splits,
+            "split_pages": plan.split_pages, "split_tokens": plan.split_tokens, "num_splits": plan.num_splits,
             "kv_bytes_per_call": kv_bytes,
         },
         "roofline": {
@@ -340,6 +340,8 @@ def main():
                 "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "rotation_copies": copies,
                 "split_pages": pl.split_pages,
+                "split_tokens": pl.split_tokens,
+                "num_splits": pl.num_splits,
             }
             print(f"[bench] config{cfg}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
             del sets, ds, wsx

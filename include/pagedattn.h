@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 #define PA_PAGE_SIZE 128
 #define PA_MAX_GQA_RATIO 16
 
@@ -96,11 +96,16 @@ typedef struct {
   int32_t split_pages;        /* pages per split; 0 lets the library choose     */
 } pa_shape_t;
 
-/* The launch plan the library derives from a shape (host arithmetic only). */
+/* The launch plan the library derives from a shape (host arithmetic only).
+ * A split is split_tokens consecutive tokens of a sequence (a multiple of 16;
+ * whole pages unless the grid would otherwise have too few waves for the
+ * context, as for small batches of short tables). */
 typedef struct {
-  int32_t split_pages;        /* pages of context each split covers             */
-  int32_t num_splits;         /* ceil(max_pages_per_seq / split_pages)          */
+  int32_t split_pages;        /* split_tokens / page_size if whole pages, else 0 */
+  int32_t num_splits;         /* >= ceil(max_pages_per_seq * page_size / split_tokens) */
   size_t workspace_bytes;     /* bytes pa_decode needs in `workspace`           */
+  int32_t split_tokens;       /* tokens of context each split covers            */
+  int32_t reserved;           /* 0                                              */
 } pa_plan_t;
 
 /* Version of this ABI (PA_ABI_VERSION of the built library). */
@@ -155,8 +160,8 @@ pa_status_t pa_decode_fp8(const pa_shape_t* shape, const void* q, const void* k_
  * range of pages and merges the partials after exchanging them). Together
  * they produce the same bits as pa_decode.
  *
- * Workspace layout (FP32), with S = plan.num_splits and T = page_size *
- * plan.split_pages: split s covers tokens [s*T, (s+1)*T) of a sequence, and
+ * Workspace layout (FP32), with S = plan.num_splits and T =
+ * plan.split_tokens: split s covers tokens [s*T, (s+1)*T) of a sequence, and
  * with s_t = scale * log2(e) * (q . k_t) over the split's tokens t < ctx,
  *   acc [B][Hq][S][D] at byte 0:        sum_t 2^(s_t - m) * v_t
  *   ml  [B][Hq][S][2] at byte align256(B*Hq*S*D*4):  { m = max_t s_t,

@@ -20,6 +20,12 @@ constexpr int64_t kTargetWaves = 4 * kTargetWorkgroups;
 // A decode split's score tile (split tokens x padded heads, FP32) lives in the
 // LDS of its wave; it is kept within 16 KiB (64 KiB per 4-wave workgroup).
 constexpr size_t kMaxWaveLdsBytes = 16 * 1024;
+// Splits are multiples of the 16-token score tile. The automatic plan shortens
+// them below a page only while a grid of whole-page splits would hold fewer
+// waves than it aims for, and never makes more than kMaxAutoSplits per sequence
+// (more splits make the merge read more partials per row).
+constexpr int kSplitQuantum = 16;
+constexpr int64_t kMaxAutoSplits = 32;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -38,41 +44,50 @@ pa_status_t check_shape(const pa_shape_t* s) {
   return PA_OK;
 }
 
-// Pages per split. Never looks at context lengths (they live on the device).
-int choose_split_pages(const pa_shape_t* s) {
+// Tokens per split. Never looks at context lengths (they live on the device).
+int choose_split_tokens(const pa_shape_t* s) {
   const int g = s->num_q_heads / s->num_kv_heads;
-  const int w = s->max_pages_per_seq;
-  int pps;
+  const int w_tokens = s->max_pages_per_seq * PA_PAGE_SIZE;
+  int st;
   if (s->split_pages > 0) {
-    pps = s->split_pages;
+    st = s->split_pages > s->max_pages_per_seq ? w_tokens : s->split_pages * PA_PAGE_SIZE;
   } else {
     const int64_t pairs = (int64_t)(s->batch > 0 ? s->batch : 1) * s->num_kv_heads;
-    const int64_t splits_wanted = (kTargetWaves + pairs - 1) / pairs;
-    pps = (int)((w + splits_wanted - 1) / splits_wanted);
+    int64_t splits_wanted = (kTargetWaves + pairs - 1) / pairs;
+    if (splits_wanted > kMaxAutoSplits) splits_wanted = kMaxAutoSplits;
+    st = (int)((w_tokens + splits_wanted - 1) / splits_wanted);
+    st = (st + kSplitQuantum - 1) / kSplitQuantum * kSplitQuantum;
+    // whole pages whenever a split spans more than one
+    if (st > PA_PAGE_SIZE) st = (st + PA_PAGE_SIZE - 1) / PA_PAGE_SIZE * PA_PAGE_SIZE;
   }
-  int cap = 1;  // largest split whose score tile fits one wave's LDS share
-  while (pa::partition_wave_lds_bytes(s->head_dim, g, cap + 1) <= kMaxWaveLdsBytes) ++cap;
-  if (pps > cap) pps = cap;
-  if (pps > w) pps = w;
-  if (pps < 1) pps = 1;
-  return pps;
+  int cap = PA_PAGE_SIZE;  // the largest page multiple whose score tile fits one wave's share
+  while (cap < w_tokens &&
+         pa::partition_wave_lds_bytes(s->head_dim, g, cap + PA_PAGE_SIZE) <= kMaxWaveLdsBytes)
+    cap += PA_PAGE_SIZE;
+  if (st > cap) st = cap;
+  if (st > w_tokens) st = w_tokens;
+  if (st < kSplitQuantum) st = kSplitQuantum;
+  return st;
 }
 
 pa_status_t make_plan(const pa_shape_t* s, pa_plan_t* p) {
-  const int pps = choose_split_pages(s);
+  const int st = choose_split_tokens(s);
   // a workgroup's waves cover heads_per_workgroup KV heads and the rest of its
   // waves consecutive splits: the split count is rounded up to fill them (the
   // extra splits start past every context and write nothing)
   const int hpw = pa::heads_per_workgroup(s->num_kv_heads);
   const int wph = pa::splits_per_workgroup(s->num_kv_heads);
-  const int splits = ((s->max_pages_per_seq + pps - 1) / pps + wph - 1) / wph * wph;
+  const int64_t w_tokens = (int64_t)s->max_pages_per_seq * PA_PAGE_SIZE;
+  const int splits = (int)(((w_tokens + st - 1) / st + wph - 1) / wph * wph);
   if ((int64_t)s->batch * (s->num_kv_heads / hpw) * (splits / wph) > INT32_MAX)
     return PA_ERR_UNSUPPORTED;
   const size_t rows = (size_t)s->batch * s->num_q_heads * splits;
-  p->split_pages = pps;
+  p->split_pages = st % PA_PAGE_SIZE == 0 ? st / PA_PAGE_SIZE : 0;
   p->num_splits = splits;
   p->workspace_bytes = align_up(rows * s->head_dim * sizeof(float), 256) +
                        align_up(rows * 2 * sizeof(float), 256);
+  p->split_tokens = st;
+  p->reserved = 0;
   return PA_OK;
 }
 
@@ -124,6 +139,8 @@ pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
   const size_t parts = (size_t)s->num_tokens * s->num_q_heads * splits;
   p->plan.split_pages = pps;
   p->plan.num_splits = splits;
+  p->plan.split_tokens = pps * PA_PAGE_SIZE;
+  p->plan.reserved = 0;
   p->plan.workspace_bytes = splits == 1 ? 0
                                         : align_up(parts * s->head_dim * sizeof(float), 256) +
                                               align_up(parts * 2 * sizeof(float), 256);
@@ -221,7 +238,7 @@ pa_status_t prepare(const pa_shape_t* shape, const void* q, const void* k_cache,
   a->head_dim = shape->head_dim;
   a->max_pages = shape->max_pages_per_seq;
   a->num_pages = shape->num_pages;
-  a->split_pages = plan.split_pages;
+  a->split_tokens = plan.split_tokens;
   a->num_splits = plan.num_splits;
   a->score_scale = scale * 1.4426950408889634f;  // natural-exp softmax computed as exp2
   a->v_scale = 1.0f;

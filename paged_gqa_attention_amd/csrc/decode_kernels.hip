@@ -10,7 +10,8 @@
 //
 // Work decomposition
 //   partition_kernel<D, G>: one wave per (sequence b, KV head h, split s); a
-//   split is `split_pages` consecutive pages of the sequence. A 4-wave
+//   split is `split_tokens` consecutive tokens of the sequence (whole pages,
+//   or a multiple of 16 tokens below a page for small grids). A 4-wave
 //   workgroup holds up to 4 adjacent KV heads of one sequence (and, with fewer
 //   KV heads, consecutive splits), so its loads cover several heads' bytes of
 //   every token row together (measured on MI355X: ~12% more bandwidth than one
@@ -68,8 +69,8 @@ struct HeadPad {
 // LDS of the partition kernel, in 4-byte words: every wave owns the score
 // tile of its split, split_tokens x GP floats.
 template <int G>
-__host__ __device__ constexpr int wave_tile_words(int split_pages) {
-  return split_pages * kPage * HeadPad<G>::value;
+__host__ __device__ constexpr int wave_tile_words(int split_tokens) {
+  return split_tokens * HeadPad<G>::value;
 }
 
 // kFp8: the K/V pools hold FP8 E4M3 codes (one byte per value) with
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int batch, int num_kv_heads, int heads_per_wg, int max_pages,
-    int num_pages, int split_pages, int num_splits, float score_scale, float v_scale) {
+    int num_pages, int split_tokens, int num_splits, float score_scale, float v_scale) {
   static_assert(D == 128 || D == 256, "head_dim");
   static_assert(G >= 1 && G <= 16, "gqa ratio");
   constexpr int ESZ = kFp8 ? 1 : 2;       // bytes per cached K/V value
@@ -129,15 +130,17 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const int h = (unit - b * num_hg) * heads_per_wg + wave % heads_per_wg;
   const int s = sg * (kWaves / heads_per_wg) + wave / heads_per_wg;
   const int num_q_heads = num_kv_heads * G;
-  const int split_tokens = split_pages * kPage;
-  float* s_tile = smem + wave * wave_tile_words<G>(split_pages);  // [token][GP]
+  float* s_tile = smem + wave * wave_tile_words<G>(split_tokens);  // [token][GP]
 
-  // The page ids of the split (lane i: page i), q and the context length load
-  // together (one memory round trip, not three). Entries past the context are
-  // read but never used.
-  const int first_page = s * split_pages;
+  // The page ids of the split (lane i: the i-th page it touches), q and the
+  // context length load together (one memory round trip, not three). Entries
+  // past the context are read but never used. split_tokens is a multiple of
+  // 16, so no 16-token tile straddles a page.
+  const int t0 = s * split_tokens;  // first token of this split
+  const int first_page = t0 / kPage;
+  const int span = (t0 % kPage + split_tokens + kPage - 1) / kPage;  // pages touched (<= 9)
   int page_id = -1;
-  if (lane < split_pages && first_page + lane < max_pages)
+  if (lane < span && first_page + lane < max_pages)
     page_id = block_table[(size_t)b * max_pages + first_page + lane];
   // A operand of the score MFMA: lane (lq, lr) holds 8 dims of q[head lr] per
   // k-step (zero rows for heads >= G), the same dims its K operand holds:
@@ -154,7 +157,6 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   }
   int ctx = context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
-  const int t0 = s * split_tokens;  // first token of this split
   const int n_s = min(ctx - t0, split_tokens);
   if (n_s <= 0) return;  // split past the context: nothing to write (no barriers below)
   page_id = (unsigned)page_id < (unsigned)num_pages ? page_id : -1;  // outside the pool: -1
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 
   // Base of the page holding local token tl (wave-uniform); bad -> pool start.
   auto page_base = [&](const void* pool, int tl, bool& bad) -> const char* {
-    const int page = __builtin_amdgcn_readlane(page_id, tl >> 7);
+    const int page = __builtin_amdgcn_readlane(page_id, (t0 + tl) / kPage - first_page);
     bad = page < 0;
     return reinterpret_cast<const char*>(pool) + (size_t)(bad ? 0 : page) * page_bytes;
   };
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     const int tl = tile * 16;
     take_turn(tl);
     const char* base = page_base(k_cache, tl, bad);
-    const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + k_lane_off;
+    const uint32_t off = (uint32_t)((t0 + tl) % kPage) * row_bytes + k_lane_off;
 #pragma unroll
     for (int j = 0; j < KL; ++j)
       buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     take_turn(tl);
     bool bad;
     const char* base = page_base(v_cache, tl, bad);  // bad pages: scores are NaN already
-    const uint32_t off = (uint32_t)(tl & (kPage - 1)) * row_bytes + v_lane_off;
+    const uint32_t off = (uint32_t)((t0 + tl) % kPage) * row_bytes + v_lane_off;
 #pragma unroll
     for (int u = 0; u < PV_U; ++u)
       buf[u] = *reinterpret_cast<const VChunk*>(base + off + (uint32_t)(u * RPI) * row_bytes);
@@ -420,12 +422,12 @@ int launch_partition_dgt(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int hpw = heads_per_workgroup(a.num_kv_heads);
   const dim3 grid(a.batch * (a.num_kv_heads / hpw) * (a.num_splits / (kWaves / hpw)));
-  const size_t lds = sizeof(float) * kWaves * wave_tile_words<G>(a.split_pages);
+  const size_t lds = sizeof(float) * kWaves * wave_tile_words<G>(a.split_tokens);
   void* args[] = {(void*)&a.q,           (void*)&a.k_cache,      (void*)&a.v_cache,
                   (void*)&a.block_table, (void*)&a.context_lens, (void*)&a.ws_acc,
                   (void*)&a.ws_ml,       (void*)&a.batch,        (void*)&a.num_kv_heads,
                   (void*)&hpw,           (void*)&a.max_pages,    (void*)&a.num_pages,
-                  (void*)&a.split_pages, (void*)&a.num_splits,   (void*)&a.score_scale,
+                  (void*)&a.split_tokens, (void*)&a.num_splits,   (void*)&a.score_scale,
                   (void*)&a.v_scale};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G, kFp8>),
                               grid, dim3(kThreads), args, lds, stream);
@@ -440,7 +442,7 @@ template <int D>
 int launch_reduce_d(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int rows = a.batch * a.num_q_heads;
-  const int split_tokens = a.split_pages * kPage;
+  const int split_tokens = a.split_tokens;
   const int max_ctx = a.max_pages * kPage;
   constexpr int RPW = kReduceThreads / (D / 4);
   void* args[] = {(void*)&a.ws_acc,      (void*)&a.ws_ml,      (void*)&a.context_lens,
@@ -463,9 +465,9 @@ typedef int (*LaunchFn)(const LaunchArgs&);
 const LaunchFn kPartition128[17] = PA_G_LIST(128);
 const LaunchFn kPartition256[17] = PA_G_LIST(256);
 
-size_t wave_tile_bytes_for(int g, int split_pages) {
+size_t wave_tile_bytes_for(int g, int split_tokens) {
   const int gp = g <= 4 ? 4 : (g <= 8 ? 8 : 16);
-  return sizeof(float) * (size_t)split_pages * kPage * gp;
+  return sizeof(float) * (size_t)split_tokens * gp;
 }
 
 }  // namespace
@@ -482,9 +484,9 @@ int heads_per_workgroup(int num_kv_heads) {
 
 int splits_per_workgroup(int num_kv_heads) { return kWaves / heads_per_workgroup(num_kv_heads); }
 
-size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_pages) {
+size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_tokens) {
   if (!has_kernels(head_dim, gqa_ratio)) return 0;
-  return wave_tile_bytes_for(gqa_ratio, split_pages);
+  return wave_tile_bytes_for(gqa_ratio, split_tokens);
 }
 
 int launch_partition(const LaunchArgs& a) {

@@ -18,7 +18,7 @@ struct LaunchArgs {
   float* ws_acc;              // f32 [B, Hq, S, D]   unnormalised split outputs
   float* ws_ml;               // f32 [B, Hq, S, 2]   (max, sum) per split, log2 units
   int batch, num_q_heads, num_kv_heads, head_dim, max_pages, num_pages;
-  int split_pages, num_splits;
+  int split_tokens, num_splits; // split s covers tokens [s * split_tokens, (s + 1) * split_tokens)
   float score_scale;          // scale * log2(e) (* k_scale for FP8), applied to q.k in FP32
   float v_scale;              // FP8 pools: multiplies the split's output sums
   bool kv_fp8;                // the pools hold FP8 E4M3 codes
@@ -35,9 +35,9 @@ bool has_kernels(int head_dim, int gqa_ratio);
 int heads_per_workgroup(int num_kv_heads);
 int splits_per_workgroup(int num_kv_heads);
 
-// Bytes of LDS one partition wave uses for a split of split_pages pages (the
+// Bytes of LDS one partition wave uses for a split of split_tokens tokens (the
 // workgroup uses four times that); 0 if no kernel exists for the shape.
-size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_pages);
+size_t partition_wave_lds_bytes(int head_dim, int gqa_ratio, int split_tokens);
 
 // Enqueue the partition kernel (split partials -> workspace) or the reduce
 // kernel (workspace -> out). Return 0 on success, else the HIP error code of

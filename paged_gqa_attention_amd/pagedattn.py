@@ -51,6 +51,8 @@ class PaPlan(ctypes.Structure):
         ("split_pages", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("split_tokens", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

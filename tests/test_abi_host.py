@@ -63,20 +63,26 @@ def test_status_strings():
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(pa.PaShape) == 8 * 4
-    assert ctypes.sizeof(pa.PaPlan) == 16
+    assert ctypes.sizeof(pa.PaPlan) == 24
+    assert pa.PaPlan.split_tokens.offset == 16
 
 
 @pytest.mark.parametrize("cfg,expect", [
-    ((2, 40, 8, 128, 2, 4), (1, 2)),       # B=2, W=2: one page per split
-    ((16, 40, 8, 128, 32, 512), (2, 16)),  # 128 (seq, kv head) pairs -> 16 waves of 256 tokens
-    ((256, 40, 8, 128, 32, 2050), (4, 8)), # one split wanted; 16 KiB wave score tile caps it at 4 pages
-    ((32, 16, 2, 256, 32, 1024), (1, 32)), # 64 pairs -> 32 splits of one page
-    ((3, 6, 2, 128, 5, 40), (1, 6)),       # 2 KV heads: 2 splits per workgroup, 5 splits -> 6
-    ((3, 3, 1, 128, 5, 40), (1, 8)),       # 1 KV head: 4 splits per workgroup, 5 splits -> 8
+    # (split_pages, num_splits, split_tokens)
+    ((2, 40, 8, 128, 2, 4), (0, 16, 16)),      # 16 (seq, kv head) pairs: 16-token splits
+    ((16, 40, 8, 128, 32, 512), (2, 16, 256)), # 128 pairs -> 16 waves of 256 tokens each
+    ((256, 40, 8, 128, 32, 2050), (4, 8, 512)),# one split wanted; 16 KiB wave score tile caps it
+    ((32, 16, 2, 256, 32, 1024), (1, 32, 128)),# 64 pairs -> 32 splits of one page
+    ((3, 6, 2, 128, 5, 40), (0, 20, 32)),      # at most 32 automatic splits: 640 / 32 tokens
+    ((3, 3, 1, 128, 5, 40), (0, 20, 32)),      # 1 KV head: 4 splits per workgroup, 20 fills 5
+    ((1, 40, 8, 128, 32, 40), (1, 32, 128)),   # batch 1 at 4096 tokens: 32 one-page splits
+    ((4, 40, 8, 128, 3, 40), (0, 24, 16)),     # 3 pages, 32 pairs: 16-token splits
 ])
 def test_plan_for_the_standard_workloads(cfg, expect):
     plan = pa.pa_plan(pa.make_shape(*cfg))
-    assert (plan.split_pages, plan.num_splits) == expect
+    assert (plan.split_pages, plan.num_splits, plan.split_tokens) == expect
+    assert plan.split_tokens % 16 == 0 and plan.reserved == 0
+    assert plan.num_splits * plan.split_tokens >= cfg[4] * 128
     B, Hq, Hkv, D, W, N = cfg
     rows = B * Hq * plan.num_splits
     r256 = lambda x: (x + 255) // 256 * 256
@@ -87,7 +93,7 @@ def test_plan_for_the_standard_workloads(cfg, expect):
 def test_plan_explicit_split_pages_and_clamp():
     for sp in (1, 2, 3, 4):
         plan = pa.pa_plan(pa.make_shape(4, 40, 8, 128, 32, 200, split_pages=sp))
-        assert plan.split_pages == sp
+        assert plan.split_pages == sp and plan.split_tokens == 128 * sp
         assert plan.num_splits == -(-32 // sp)
     # a split whose score tile would exceed one wave's 16 KiB of LDS is
     # clamped: G=5 pads to 8 heads, 4 KiB per page

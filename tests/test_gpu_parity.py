@@ -67,6 +67,31 @@ def test_split_sizes(G, Hkv, split_pages):
     assert_parity(run_gpu(w, split_pages=split_pages), run_oracle(w), f"split {split_pages}")
 
 
+# small grids get splits shorter than a page (multiples of 16 tokens), so a
+# split can start mid-page and span two pages; ragged lengths around 16-token
+# and page boundaries, with poison in every slot no sequence reads
+@pytest.mark.parametrize("B,Hq,Hkv,D,W,ctx", [
+    (3, 40, 8, 128, 3, [1, 17, 383]),
+    (2, 16, 2, 256, 5, [640, 129]),
+    (1, 8, 1, 128, 7, [881]),
+    (4, 24, 2, 256, 2, [0, 16, 255, 32]),
+])
+def test_sub_page_splits(B, Hq, Hkv, D, W, ctx):
+    from paged_gqa_attention_amd import pagedattn as pa
+    w = workloads.build(B, Hq, Hkv, D, ctx, seed=200 + B + W, max_pages=W, pool="permutation")
+    w = workloads.poison_unused(w)
+    plan = pa.pa_plan(pa.shape_of(w.q, w.k_cache, w.block_table))
+    announce(f"sub-page splits B={B} {Hq}/{Hkv}/{D} W={W}: {plan.split_tokens} tokens x "
+             f"{plan.num_splits}")
+    assert plan.split_tokens < 128
+    out = run_gpu(w)
+    ref = run_oracle(w)
+    for b, n in enumerate(ctx):
+        if n == 0:
+            assert torch.all(out[b] == 0)
+    assert_parity(out, ref, f"sub-page B={B} W={W}")
+
+
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("G", list(range(1, 17)))
 def test_every_gqa_ratio(D, G):
@@ -234,7 +259,7 @@ def test_merge_stage_on_oracle_partials():
     w = workloads.build(B, Hq, Hkv, D, ctx, seed=61, max_pages=32, pool="packed")
     shape = pa.shape_of(w.q, w.k_cache, w.block_table, split_pages=3)
     plan = pa.pa_plan(shape)
-    S, T = plan.num_splits, 128 * plan.split_pages
+    S, T = plan.num_splits, plan.split_tokens
     acc = np.zeros((B, Hq, S, D), np.float32)
     ml = np.zeros((B, Hq, S, 2), np.float32)
     kc = w.k_cache.float().numpy().astype(np.float64)
