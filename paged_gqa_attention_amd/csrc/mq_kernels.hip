@@ -53,17 +53,19 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef char __attribute__((address_space(3))) lds_char;
 
 // Workgroup shapes, by RT = 16-row tiles per workgroup (1, 2, 4 or 8):
-//   TPW  row tiles per wave: 1, except 2 for head_dim 256 at RT 8 (its
-//        registers allow 4 waves of 32 rows, not 8 waves of 16); head_dim 128
-//        at RT 8 runs 8 waves (512 threads), so that every staged K/V chunk
-//        feeds 128 rows and the cache is re-read half as often as at RT 4
+//   TPW  row tiles per wave: 1. The kernel also takes 2 (each LDS operand
+//        read then serves 32 rows), but at head_dim 256 that needs 373 VGPRs,
+//        one wave per SIMD, and measured 12% slower on MI355X than 8 waves of
+//        16 rows at 238 VGPRs. RT 8 runs 8 waves (512 threads), so that every
+//        staged K/V chunk feeds 128 rows and the cache is re-read half as
+//        often as at RT 4
 //   WR   waves along the rows (RT / TPW)
 //   KS   KV streams, 4 waves in all (head_dim 256 always has RT >= 2)
 //   NBUF LDS stages: 2 (one barrier per iteration, the next stage is written
 //        while the current one is read) where both fit in 64 KiB, else 1
 //   PF   prefetch distance: the loads of iteration i + PF go out right after
 //        iteration i's registers are written to LDS (PF register slots)
-__host__ __device__ constexpr int mq_tpw(int d, int rt) { return rt == 8 && d == 256 ? 2 : 1; }
+__host__ __device__ constexpr int mq_tpw(int, int) { return 1; }
 __host__ __device__ constexpr int mq_streams(int d, int rt) {
   return rt >= 4 ? 1 : (rt == 2 ? 2 : 4);
 }
