@@ -114,6 +114,7 @@ pa_status_t check_mq_shape(const pa_mq_shape_t* s) {
 struct MqPlan {
   pa_plan_t plan;
   int row_tiles, row_blocks;
+  int order_by_work;  // MFMA-bound rows and at most 64 sequences: longest first
 };
 
 pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
@@ -127,14 +128,11 @@ pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
   if (s->split_pages > 0) {
     pps = s->split_pages;
   } else {
-    // Split the context only while the rows alone give too few workgroups.
-    // MFMA-bound rows (a full 128-row tile per KV head) gain from twice the
-    // workgroups of the HBM-bound case while the rows alone give fewer than
-    // two per CU (measured on MI355X: 257 rows x 8 heads at D 256, 136 row
-    // blocks, ran 87 us with 8 splits against 97 us with 4).
-    const int64_t target =
-        rows >= 128 && base < kTargetWorkgroups ? 2 * kTargetWorkgroups : kTargetWorkgroups;
-    const int64_t splits_wanted = (target + base - 1) / base;
+    // Split the context only while the rows alone give too few workgroups
+    // (measured on MI355X with longest-first dispatch: 257 rows x 8 heads at
+    // D 256, 136 row blocks, ran 65 us with 4 splits, 73 us with 8, 82 us
+    // unsplit; 512-row chunks, 640 row blocks, are fastest unsplit).
+    const int64_t splits_wanted = (kTargetWorkgroups + base - 1) / base;
     pps = (int)((w + splits_wanted - 1) / splits_wanted);
   }
   if (pps > w) pps = w;
@@ -152,6 +150,7 @@ pa_status_t make_mq_plan(const pa_mq_shape_t* s, MqPlan* p) {
                                               align_up(parts * 2 * sizeof(float), 256);
   p->row_tiles = rt;
   p->row_blocks = row_blocks;
+  p->order_by_work = rows >= 128 && s->batch <= 64 ? 1 : 0;
   return PA_OK;
 }
 
@@ -409,6 +408,7 @@ pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const voi
   a.num_pages = shape->num_pages;
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
+  a.order_by_work = p.order_by_work;
   a.split_pages = p.plan.split_pages;
   a.num_splits = p.plan.num_splits;
   a.score_scale = scale * 1.4426950408889634f;

@@ -74,6 +74,7 @@ struct MqLaunchArgs {
   int max_pages, num_pages;
   int row_tiles;               // 16-row tiles per workgroup: 1, 2, 4 or 8
   int row_blocks;              // workgroups along the rows of one (sequence, KV head)
+  int order_by_work;           // 1: dispatch sequences longest first (batch <= 64)
   int split_pages, num_splits;
   float score_scale;           // scale * log2(e)
   void* stream;                // hipStream_t

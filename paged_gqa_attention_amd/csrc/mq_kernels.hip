@@ -138,6 +138,48 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_char* base, uint32_t of
   return __builtin_bit_cast(u32x2, r);
 }
 
+// The (sequence, KV head, rest) unit of this workgroup, where rest counts the
+// row blocks and splits of the pair. By default (sequence, KV head) pairs vary
+// fastest. With order_by_work (few sequences, MFMA-bound rows) the sequences go
+// out longest first: a sequence's estimated work is its query rows times its
+// context tokens, and workgroup x takes the sequence of rank x / units_per_seq
+// (ties by index). Measured on MI355X: 512-token prefill chunks over contexts
+// of 613..3660 tokens otherwise ran a second round of long workgroups while
+// half the slots sat idle. Needs batch <= 64 (one lane per sequence).
+__device__ __forceinline__ void workgroup_unit(int order_by_work, int batch, int num_kv_heads,
+                                               int units_per_pair,
+                                               const int32_t* __restrict__ context_lens,
+                                               const int32_t* __restrict__ query_start, int& b,
+                                               int& h, int& rest) {
+  if (!order_by_work) {
+    const int num_pairs = batch * num_kv_heads;
+    const int pair = blockIdx.x % num_pairs;
+    rest = blockIdx.x / num_pairs;
+    h = pair % num_kv_heads;
+    b = pair / num_kv_heads;
+    return;
+  }
+  const int per_seq = num_kv_heads * units_per_pair;
+  const int rank = blockIdx.x / per_seq;
+  const int x = blockIdx.x - rank * per_seq;
+  h = x % num_kv_heads;
+  rest = x / num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  float w = -1.f;  // lanes past the batch rank last
+  if (lane < batch) {
+    const int c = context_lens[lane];
+    const int lq = query_start[lane + 1] - query_start[lane];
+    w = c > 0 && lq > 0 ? (float)c * (float)lq : 0.f;
+  }
+  int my_rank = 0;
+  for (int i = 0; i < batch; ++i) {
+    const float wi = __shfl(w, i);
+    my_rank += wi > w || (wi == w && i < lane) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(lane < batch && my_rank == rank);
+  b = __builtin_amdgcn_readfirstlane(hit ? __ffsll((long long)hit) - 1 : 0);
+}
+
 template <int D, int RT>
 __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -145,7 +187,8 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
     uint16_t* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int batch, int num_tokens, int num_kv_heads, int gqa, int max_pages, int num_pages,
-    int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale) {
+    int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale,
+    int order_by_work) {
   static_assert(D == 128 || D == 256, "head_dim");
   constexpr int TPW = mq_tpw(D, RT);
   constexpr int WR = RT / TPW;
@@ -172,13 +215,11 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
   // 1-D grid, (sequence, KV head) pair fastest, then row block, then split.
   // Row blocks go from the last one down: later query tokens see more of the
   // context, so the longest workgroups are dispatched first.
-  const int num_pairs = batch * num_kv_heads;
-  const int pair = blockIdx.x % num_pairs;
-  const int rest = blockIdx.x / num_pairs;
+  int b, h, rest;
+  workgroup_unit(order_by_work, batch, num_kv_heads, row_blocks * num_splits, context_lens,
+                 query_start, b, h, rest);
   const int rb = row_blocks - 1 - rest % row_blocks;
   const int s = rest / row_blocks;
-  const int h = pair % num_kv_heads;
-  const int b = pair / num_kv_heads;
   const int num_q_heads = num_kv_heads * gqa;
 
   // A sequence whose query range is not inside [0, num_tokens] or is longer
@@ -536,7 +577,8 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
     uint16_t* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int batch, int num_tokens, int num_kv_heads, int gqa, int max_pages, int num_pages,
-    int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale) {
+    int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale,
+    int order_by_work) {
   constexpr int D = 128;
   constexpr int NT = kM32Threads;
   constexpr int KD = D / 16;                // k-steps of the 32x32x16 score MFMA
@@ -554,13 +596,11 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem_mq[];
   lds_char* lds = (lds_char*)smem_mq;
 
-  const int num_pairs = batch * num_kv_heads;
-  const int pair = blockIdx.x % num_pairs;
-  const int rest = blockIdx.x / num_pairs;
+  int b, h, rest;
+  workgroup_unit(order_by_work, batch, num_kv_heads, row_blocks * num_splits, context_lens,
+                 query_start, b, h, rest);
   const int rb = row_blocks - 1 - rest % row_blocks;  // longest row blocks first
   const int s = rest / row_blocks;
-  const int h = pair % num_kv_heads;
-  const int b = pair / num_kv_heads;
   const int num_q_heads = num_kv_heads * gqa;
 
   const int qs0 = query_start[b];
@@ -833,7 +873,7 @@ int launch_mq_drt(const MqLaunchArgs& a) {
                   (void*)&a.batch,       (void*)&a.num_tokens,    (void*)&a.num_kv_heads,
                   (void*)&gqa,           (void*)&a.max_pages,     (void*)&a.num_pages,
                   (void*)&a.max_query_len, (void*)&a.row_blocks,  (void*)&a.split_pages,
-                  (void*)&a.num_splits,  (void*)&a.score_scale};
+                  (void*)&a.num_splits,  (void*)&a.score_scale,   (void*)&a.order_by_work};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq_kernel<D, RT>), grid,
                               dim3(64 * mq_waves(D, RT)), args, mq_lds_bytes(D, RT), stream);
 }
@@ -848,7 +888,7 @@ int launch_mq32(const MqLaunchArgs& a) {
                   (void*)&a.batch,       (void*)&a.num_tokens,    (void*)&a.num_kv_heads,
                   (void*)&gqa,           (void*)&a.max_pages,     (void*)&a.num_pages,
                   (void*)&a.max_query_len, (void*)&a.row_blocks,  (void*)&a.split_pages,
-                  (void*)&a.num_splits,  (void*)&a.score_scale};
+                  (void*)&a.num_splits,  (void*)&a.score_scale,   (void*)&a.order_by_work};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq32_kernel), grid,
                               dim3(kM32Threads), args, mq32_lds_bytes(), stream);
 }

@@ -240,8 +240,8 @@ def test_mq_shape_struct():
     # 512-token chunks: 2560 rows -> 20 row blocks of 128; 640 workgroups: one split
     (dict(B=4, T=2048, L=512), (32, 1)),
     # (16, 2) head_dim 256, 257 rows x G 8 = 2056 rows -> 17 row blocks; B=4: 136
-    # MFMA-bound workgroups aim for 1024: 8 splits
-    (dict(B=4, T=1028, L=257, Hq=16, Hkv=2, D=256, N=128), (4, 8)),
+    # workgroups want 4 splits
+    (dict(B=4, T=1028, L=257, Hq=16, Hkv=2, D=256, N=128), (8, 4)),
     # MFMA-bound but 640 workgroups already: no split
     (dict(B=4, T=2048, L=512, Hq=40, Hkv=8), (32, 1)),
     # one query row: decode-sized launch, 32 splits of 1 page

@@ -185,6 +185,32 @@ def test_bad_page_only_affects_rows_that_see_it():
     assert_parity(out[:2].to(torch.bfloat16), ref[:2], "mq bad page rows 0-1")
 
 
+@pytest.mark.parametrize("B", [6, 65])
+def test_longest_first_dispatch_ragged(B):
+    # 26 query tokens x G 5 = 130 rows per KV head: MFMA-bound rows, so batches
+    # of up to 64 sequences go out longest first (65 keep the default order);
+    # ragged query lengths and contexts, and with 6 sequences one bad context
+    # (ranked first by its huge length, its rows must still be NaN)
+    rng = np.random.default_rng(B)
+    lq = [26 if i % 3 else int(rng.integers(1, 27)) for i in range(B)]
+    ctx = [int(rng.integers(q, 700)) for q in lq]
+    announce(f"mq longest-first dispatch B={B}")
+    w = workloads.build_mq(lq, ctx, 40, 8, 128, seed=300 + B, max_pages=6, pool="permutation")
+    ref = oracle_mq(w)
+    if B == 6:
+        bad = w.context_lens.clone()
+        bad[2] = 10 ** 6
+        w2 = workloads.MqWorkload(w.name, w.q, w.k_cache, w.v_cache, w.block_table, bad,
+                                  w.query_start, w.scale)
+        out = run_mq(w2)
+        qs = w.query_start.tolist()
+        assert torch.isnan(out[qs[2]:qs[3]].float()).all()
+        keep = torch.ones(w.num_tokens, dtype=torch.bool)
+        keep[qs[2]:qs[3]] = False
+        assert_parity(out[keep], ref[keep.numpy()], "mq ordered, bad context")
+    assert_parity(run_mq(w), ref, f"mq ordered B={B}")
+
+
 def test_shared_prefix_pages():
     # two sequences share their first pages (a common prefix), then diverge
     announce("mq shared prefix")
