@@ -247,6 +247,50 @@ def test_workspace_reuse_across_shapes():
     assert torch.equal(a, b)
 
 
+def test_maximum_batch():
+    # the largest batch the boundary accepts (65,535 sequences, one page each,
+    # all sharing a 64-page pool); contexts 0..128; sampled rows against the
+    # oracle one sequence at a time, every empty sequence exactly zero
+    import oracle
+    from paged_gqa_attention_amd import pagedattn as pa
+    B, Hq, Hkv, D, N = 65535, 8, 1, 128, 64
+    announce("maximum batch 65535")
+    gen = torch.Generator().manual_seed(71)
+    q = torch.randn(B, Hq, D, generator=gen).to(torch.bfloat16)
+    kc = torch.randn(N, 128, Hkv, D, generator=gen).to(torch.bfloat16)
+    vc = torch.randn(N, 128, Hkv, D, generator=gen).to(torch.bfloat16)
+    bt = (torch.arange(B, dtype=torch.int32) % N).reshape(B, 1)
+    ctx = torch.randint(0, 129, (B,), generator=gen, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(D)
+    plan = pa.pa_plan(pa.shape_of(q, kc, bt))
+    announce(f"  plan: {plan.split_tokens} tokens x {plan.num_splits} splits")
+    dev = "cuda:0"
+    out = pa.pa_decode(q.to(dev), kc.to(dev), vc.to(dev), bt.to(dev), ctx.to(dev),
+                       scale=scale).cpu()
+    torch.cuda.synchronize()
+    assert torch.all(out[ctx == 0] == 0)
+    rng = np.random.default_rng(71)
+    rows = sorted(set(rng.integers(0, B, 256).tolist()) | {0, B - 1})
+    ref = np.stack([oracle.paged_decode_attention(q[b:b + 1], kc, vc, bt[b:b + 1],
+                                                  ctx[b:b + 1], scale)[0] for b in rows])
+    assert_parity(out[rows], ref, "maximum batch (sampled)")
+
+
+def test_maximum_block_table_width():
+    # a block table 2^20 pages wide (the boundary's limit: contexts up to 2^27
+    # tokens), one sequence of 200,000 tokens and one of 777; the plan's splits
+    # cover the whole width and the merge sees ~200 of them for the long row
+    from paged_gqa_attention_amd import pagedattn as pa
+    W = 1 << 20
+    announce("block table width 2^20")
+    w = workloads.build(2, 4, 1, 128, [200_000, 777], seed=72, max_pages=W, pool="packed")
+    plan = pa.pa_plan(pa.shape_of(w.q, w.k_cache, w.block_table))
+    announce(f"  plan: {plan.split_tokens} tokens x {plan.num_splits} splits, "
+             f"{plan.workspace_bytes / 1e6:.0f} MB workspace")
+    assert plan.num_splits * plan.split_tokens >= W * 128
+    assert_parity(run_gpu(w), run_oracle(w), "table width 2^20")
+
+
 def test_merge_stage_on_oracle_partials():
     # the reduce kernel alone: the oracle's per-split partials (FP64, rounded to
     # FP32, maxima converted to log2 units) go into the documented workspace
