@@ -411,27 +411,36 @@ def main():
         del kc, vc
 
         # multi-query attention (multi-token decode, chunked prefill): cold
-        # rotation over 4 copies of each workload's cache
-        for name in ("mtp4", "prefill512", "wide257"):
+        # rotation over 4 copies of each workload's cache; BF16 pools, then the
+        # same workloads over FP8-E4M3 pools (half the cache bytes)
+        for name, fp8 in (("mtp4", False), ("prefill512", False), ("wide257", False),
+                          ("mtp4", True), ("prefill512", True)):
             wm = workloads.mq_config(name)
             shp = pa.mq_shape_of(wm.q, wm.k_cache, wm.block_table, wm.max_query_len)
             pl = pa.pa_mq_plan(shp)
             wsx = torch.empty(max(256, pl.workspace_bytes), dtype=torch.uint8, device=dev)
             btx, ctxx, qsx = (wm.block_table.to(dev), wm.context_lens.to(dev),
                               wm.query_start.to(dev))
+            f8 = workloads.quantize_fp8(wm) if fp8 else None
             keep, margs = [], []
             for _ in range(4):
-                qx, kx, vx = wm.q.to(dev), wm.k_cache.to(dev), wm.v_cache.to(dev)
+                qx = wm.q.to(dev)
+                kx, vx = ((f8.k_codes.to(dev), f8.v_codes.to(dev)) if fp8 else
+                          (wm.k_cache.to(dev), wm.v_cache.to(dev)))
                 ox = torch.empty_like(qx)
                 keep.append((qx, kx, vx, ox))
+                scales = (ctypes.c_float(f8.k_scale), ctypes.c_float(f8.v_scale)) if fp8 else ()
                 margs.append((ctypes.byref(shp), qx.data_ptr(), kx.data_ptr(), vx.data_ptr(),
-                              btx.data_ptr(), ctxx.data_ptr(), qsx.data_ptr(),
+                              *scales, btx.data_ptr(), ctxx.data_ptr(), qsx.data_ptr(),
                               ctypes.c_float(wm.scale), ox.data_ptr(), wsx.data_ptr(),
                               wsx.numel(), stream))
-            ms = timed(torch, [lambda a=a: pa.lib.pa_mq_attention(*a) for a in margs], 100, 8)
-            by, fl = wm.kv_bytes(), wm.flops()
+            fn = pa.lib.pa_mq_attention_fp8 if fp8 else pa.lib.pa_mq_attention
+            ms = timed(torch, [lambda a=a: fn(*a) for a in margs], 100, 8)
+            by, fl = wm.kv_bytes() // (2 if fp8 else 1), wm.flops()
+            name = f"fp8_{name}" if fp8 else name
             extra[f"mq_{name}"] = {
-                "description": workloads.MQ_DESCRIPTIONS[name],
+                "description": workloads.MQ_DESCRIPTIONS[name.replace("fp8_", "")] +
+                               (", FP8-E4M3 pools with per-tensor scales" if fp8 else ""),
                 "us_per_call": round(ms * 1e3, 2),
                 "kv_bytes_per_call": by,
                 "kv_gbs": round(by / (ms * 1e-3) / 1e9, 1),

@@ -268,6 +268,19 @@ pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const voi
                             float scale, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Multi-query attention over FP8 pools: k_cache and v_cache hold FP8 E4M3
+ * codes (as for pa_decode_fp8: one byte per value in [page, token, kv_head,
+ * dim] order, 16-byte aligned) standing for code * k_scale and code * v_scale
+ * (finite FP32 scales). Everything else is as for pa_mq_attention. A
+ * deployment that keeps its KV cache in fp8_e4m3 (the dtype the orcarouter
+ * page measures) runs its chunked prefill and multi-token decode over the
+ * same pools as its single-token decode. */
+pa_status_t pa_mq_attention_fp8(const pa_mq_shape_t* shape, const void* q, const void* k_cache,
+                                const void* v_cache, float k_scale, float v_scale,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                const int32_t* query_start, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- attention prologue: QK-norm, NeoX RoPE, KV write ----------------------
  * The steps between the QKV projection and attention, fused in one kernel
  * ("Qwen 3" TensorSharp docs, section 3 "Forward graph" and section 4.1

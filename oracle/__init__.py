@@ -15,6 +15,7 @@ from .decode import (  # noqa: F401
     paged_decode_attention_fp8,
     paged_kv_write,
     paged_multi_query_attention,
+    paged_multi_query_attention_fp8,
     partial_attention,
 )
 from .prologue import (  # noqa: F401

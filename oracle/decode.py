@@ -354,3 +354,18 @@ def paged_multi_query_attention(q, k_cache, v_cache, block_table, context_lens, 
                 h = hq // G
                 out[r, hq] = attend(q[r, hq], K[:n, h, :], V[:n, h, :], s64)
     return out
+
+
+def paged_multi_query_attention_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table,
+                                    context_lens, query_start, scale):
+    """Multi-query attention over FP8-E4M3 K/V pools with per-tensor FP32 scales.
+
+    K = decode(k_codes) * k_scale and V = decode(v_codes) * v_scale, as in
+    ``paged_decode_attention_fp8``, then ``paged_multi_query_attention``: a
+    cache kept in fp8_e4m3 (the KV dtype the orcarouter page measures) is read
+    by chunked prefill and multi-token decode as well as by single-token
+    decode.
+    """
+    k = decode_fp8_e4m3(k_codes) * float(np.float32(k_scale))
+    v = decode_fp8_e4m3(v_codes) * float(np.float32(v_scale))
+    return paged_multi_query_attention(q, k, v, block_table, context_lens, query_start, scale)

@@ -252,6 +252,67 @@ pa_status_t prepare(const pa_shape_t* shape, const void* q, const void* k_cache,
   return PA_OK;
 }
 
+// The multi-query call over BF16 or FP8 pools (validation, plan, launches).
+pa_status_t mq_call(const pa_mq_shape_t* shape, const void* q, const void* k_cache,
+                    const void* v_cache, bool kv_fp8, float k_scale, float v_scale,
+                    const int32_t* block_table, const int32_t* context_lens,
+                    const int32_t* query_start, float scale, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_mq_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0 || shape->num_tokens == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !query_start || !out)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      ((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)query_start & 3u))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale) || !isfinite(k_scale) || !isfinite(v_scale)) return PA_ERR_INVALID_ARGUMENT;
+  MqPlan p;
+  st = make_mq_plan(shape, &p);
+  if (st != PA_OK) return st;
+  if (p.plan.workspace_bytes > 0) {
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.plan.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const size_t parts = (size_t)shape->num_tokens * shape->num_q_heads * p.plan.num_splits;
+  pa::MqLaunchArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = static_cast<uint16_t*>(out);
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = p.plan.workspace_bytes > 0
+                ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align_up(parts * shape->head_dim * sizeof(float), 256))
+                : nullptr;
+  a.batch = shape->batch;
+  a.num_tokens = shape->num_tokens;
+  a.max_query_len = shape->max_query_len;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  a.row_tiles = p.row_tiles;
+  a.row_blocks = p.row_blocks;
+  a.order_by_work = p.order_by_work;
+  a.split_pages = p.plan.split_pages;
+  a.num_splits = p.plan.num_splits;
+  // FP8: K = code * k_scale enters the logits linearly, folded into the score scale
+  a.score_scale = (kv_fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
+  a.v_scale = kv_fp8 ? v_scale : 1.0f;
+  a.kv_fp8 = kv_fp8;
+  a.stream = stream;
+  if (pa::launch_mq(a) != 0) return PA_ERR_LAUNCH;
+  if (a.num_splits == 1) return PA_OK;
+  return pa::launch_mq_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,61 +422,23 @@ pa_status_t pa_mq_plan(const pa_mq_shape_t* shape, pa_plan_t* plan) {
   return pst;
 }
 
+
 pa_status_t pa_mq_attention(const pa_mq_shape_t* shape, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,
                             const int32_t* context_lens, const int32_t* query_start,
                             float scale, void* out, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  pa_status_t st = check_mq_shape(shape);
-  if (st != PA_OK) return st;
-  if (shape->batch == 0 || shape->num_tokens == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !query_start || !out)
-    return PA_ERR_NULL_POINTER;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      ((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
-      ((uintptr_t)query_start & 3u))
-    return PA_ERR_INVALID_ARGUMENT;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
-  MqPlan p;
-  st = make_mq_plan(shape, &p);
-  if (st != PA_OK) return st;
-  if (p.plan.workspace_bytes > 0) {
-    if (!workspace) return PA_ERR_NULL_POINTER;
-    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < p.plan.workspace_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
-  }
-  const size_t parts = (size_t)shape->num_tokens * shape->num_q_heads * p.plan.num_splits;
-  pa::MqLaunchArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
-  a.block_table = block_table;
-  a.context_lens = context_lens;
-  a.query_start = query_start;
-  a.out = static_cast<uint16_t*>(out);
-  a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = p.plan.workspace_bytes > 0
-                ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           align_up(parts * shape->head_dim * sizeof(float), 256))
-                : nullptr;
-  a.batch = shape->batch;
-  a.num_tokens = shape->num_tokens;
-  a.max_query_len = shape->max_query_len;
-  a.num_q_heads = shape->num_q_heads;
-  a.num_kv_heads = shape->num_kv_heads;
-  a.head_dim = shape->head_dim;
-  a.max_pages = shape->max_pages_per_seq;
-  a.num_pages = shape->num_pages;
-  a.row_tiles = p.row_tiles;
-  a.row_blocks = p.row_blocks;
-  a.order_by_work = p.order_by_work;
-  a.split_pages = p.plan.split_pages;
-  a.num_splits = p.plan.num_splits;
-  a.score_scale = scale * 1.4426950408889634f;
-  a.stream = stream;
-  if (pa::launch_mq(a) != 0) return PA_ERR_LAUNCH;
-  if (a.num_splits == 1) return PA_OK;
-  return pa::launch_mq_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+  return mq_call(shape, q, k_cache, v_cache, false, 1.0f, 1.0f, block_table, context_lens,
+                 query_start, scale, out, workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_mq_attention_fp8(const pa_mq_shape_t* shape, const void* q, const void* k_cache,
+                                const void* v_cache, float k_scale, float v_scale,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                const int32_t* query_start, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return mq_call(shape, q, k_cache, v_cache, true, k_scale, v_scale, block_table, context_lens,
+                 query_start, scale, out, workspace, workspace_bytes, stream);
 }
 
 pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* q, const void* k,

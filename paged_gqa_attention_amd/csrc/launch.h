@@ -62,8 +62,8 @@ int launch_kv_write(const KvWriteArgs& a);
 // Arguments of a multi-query call, already validated on the host.
 struct MqLaunchArgs {
   const uint16_t* q;           // bf16 [T, Hq, D]
-  const uint16_t* k_cache;     // bf16 [N, P, Hkv, D]
-  const uint16_t* v_cache;     // bf16 [N, P, Hkv, D]
+  const void* k_cache;         // bf16 or fp8-e4m3 [N, P, Hkv, D]
+  const void* v_cache;         // bf16 or fp8-e4m3 [N, P, Hkv, D]
   const int32_t* block_table;  // int32 [B, W]
   const int32_t* context_lens; // int32 [B]
   const int32_t* query_start;  // int32 [B + 1]
@@ -76,7 +76,9 @@ struct MqLaunchArgs {
   int row_blocks;              // workgroups along the rows of one (sequence, KV head)
   int order_by_work;           // 1: dispatch sequences longest first (batch <= 64)
   int split_pages, num_splits;
-  float score_scale;           // scale * log2(e)
+  float score_scale;           // scale * log2(e) (* k_scale for FP8)
+  float v_scale;               // FP8 pools: multiplies the output sums (1 for BF16)
+  bool kv_fp8;                 // the pools hold FP8 E4M3 codes
   void* stream;                // hipStream_t
 };
 

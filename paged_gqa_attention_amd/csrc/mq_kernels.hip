@@ -38,6 +38,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -138,6 +140,24 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_char* base, uint32_t of
   return __builtin_bit_cast(u32x2, r);
 }
 
+// K/V staging from the pools. BF16 pools: 16 bytes (8 values) per chunk.
+// FP8 E4M3 pools (kFp8): the same 8 values are 8 bytes of codes, widened to
+// BF16 exactly (every E4M3 value is a BF16 value) before they go to LDS, so
+// the LDS layout and the MFMAs are those of the BF16 path; k_scale is folded
+// into the score scale on the host and v_scale multiplies the output sums.
+template <bool kFp8>
+using MqStage = typename std::conditional<kFp8, u32x2, u32x4>::type;
+
+template <bool kFp8>
+__device__ __forceinline__ MqStage<kFp8> load_stage(const void* pool, size_t elem) {
+  if constexpr (kFp8)
+    return *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(pool) + elem);
+  else
+    return load16(reinterpret_cast<const uint16_t*>(pool) + elem);
+}
+__device__ __forceinline__ u32x4 widen_stage(u32x4 v) { return v; }
+__device__ __forceinline__ u32x4 widen_stage(u32x2 v) { return fp8x8_to_bf16x8(v[0], v[1]); }
+
 // The (sequence, KV head, rest) unit of this workgroup, where rest counts the
 // row blocks and splits of the pair. By default (sequence, KV head) pairs vary
 // fastest. With order_by_work (few sequences, MFMA-bound rows) the sequences go
@@ -180,15 +200,15 @@ __device__ __forceinline__ void workgroup_unit(int order_by_work, int batch, int
   b = __builtin_amdgcn_readfirstlane(hit ? __ffsll((long long)hit) - 1 : 0);
 }
 
-template <int D, int RT>
+template <int D, int RT, bool kFp8>
 __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
     uint16_t* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int batch, int num_tokens, int num_kv_heads, int gqa, int max_pages, int num_pages,
     int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale,
-    int order_by_work) {
+    float v_scale, int order_by_work) {
   static_assert(D == 128 || D == 256, "head_dim");
   constexpr int TPW = mq_tpw(D, RT);
   constexpr int WR = RT / TPW;
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
   const int32_t* bt_row = block_table + (size_t)b * max_pages;
   const int n_it = t_end > t_begin ? (t_end - t_begin + IT - 1) / IT : 0;
 
-  u32x4 stg[PF][UPT];
+  MqStage<kFp8> stg[PF][UPT];
   bool stg_bad[PF];
 
   // The page ids of the workgroup's range (at most kMqMaxSplitPages, the
@@ -319,8 +339,8 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
       const int u = (tid + NT * k) % (NT * UPT / 2);
       const int c = u % CPR;
       const int tr = u / CPR;  // token of the iteration: stream * 32 + row
-      const uint16_t* pool = k < UPT / 2 ? k_cache : v_cache;
-      stg[slot][k] = load16(pool + base + (size_t)tr * row_elems + 8 * c);
+      stg[slot][k] = load_stage<kFp8>(k < UPT / 2 ? k_cache : v_cache,
+                                      base + (size_t)tr * row_elems + 8 * c);
     }
   };
   // Register slot -> LDS stage of iteration it.
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
         const int tr = u / CPR;
         const uint32_t off = (is_k ? 0u : (uint32_t)(KS * TILE)) + (uint32_t)((tr / kChunk) * TILE) +
                              (is_k ? k_off<D>(tr % kChunk, c) : v_off<D>(tr % kChunk, c));
-        *(u32x4 __attribute__((address_space(3)))*)(stage + off) = stg[slot][k];
+        *(u32x4 __attribute__((address_space(3)))*)(stage + off) = widen_stage(stg[slot][k]);
       }
       return;
     }
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
       const int tr = u / CPR;
       const int st = tr / kChunk;
       const int r = tr % kChunk;
-      u32x4 v = stg[slot][k];
+      u32x4 v = widen_stage(stg[slot][k]);
       // rows past the range hold other data (NaN poison included): zero them,
       // so that P = 0 times V stays 0. A bad page reads as NaN K (the rows
       // that see it become NaN) and zero V (the rows that do not see it are
@@ -542,13 +562,13 @@ __global__ __launch_bounds__(64 * mq_waves(D, RT)) void mq_kernel(
       } else {
         const float inv = l_run[tt] > 0.f ? 1.f / l_run[tt] : 0.f;  // no visible token: zeros
 #pragma unroll
-        for (int db = 0; db < DB; ++db) store_bf16x4(dst + 16 * db, o[tt][db] * inv);
+        for (int db = 0; db < DB; ++db) store_bf16x4(dst + 16 * db, o[tt][db] * (inv * v_scale));
       }
     } else {
       const size_t slot = orow[tt] * num_splits + s;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4*>(ws_acc + slot * D + 16 * db + 4 * lq) = o[tt][db];
+        *reinterpret_cast<f32x4*>(ws_acc + slot * D + 16 * db + 4 * lq) = o[tt][db] * v_scale;
       if (lq == 0) *reinterpret_cast<float2*>(ws_ml + slot * 2) = make_float2(m_run[tt], l_run[tt]);
     }
   }
@@ -571,14 +591,15 @@ __host__ __device__ constexpr int mq32_lds_bytes() {
   return mq32_stage_bytes() + 4 * kMqMaxSplitPages;
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
     uint16_t* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int batch, int num_tokens, int num_kv_heads, int gqa, int max_pages, int num_pages,
     int max_query_len, int row_blocks, int split_pages, int num_splits, float score_scale,
-    int order_by_work) {
+    float v_scale, int order_by_work) {
   constexpr int D = 128;
   constexpr int NT = kM32Threads;
   constexpr int KD = D / 16;                // k-steps of the 32x32x16 score MFMA
@@ -647,7 +668,7 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
   const int32_t* bt_row = block_table + (size_t)b * max_pages;
   const int n_it = t_end > t_begin ? (t_end - t_begin + IT - 1) / IT : 0;
 
-  u32x4 stg[PF][UPT];
+  MqStage<kFp8> stg[PF][UPT];
   bool stg_bad[PF];
   int* s_pages = reinterpret_cast<int*>(smem_mq + mq32_stage_bytes());
   {
@@ -668,8 +689,8 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = (tid + NT * k) % (NT * UPT / 2);
-      const uint16_t* pool = k < UPT / 2 ? k_cache : v_cache;
-      stg[slot][k] = load16(pool + base + (size_t)(u / CPR) * row_elems + 8 * (u % CPR));
+      stg[slot][k] = load_stage<kFp8>(k < UPT / 2 ? k_cache : v_cache,
+                                      base + (size_t)(u / CPR) * row_elems + 8 * (u % CPR));
     }
   };
   auto commit = [&](int it, int slot) {
@@ -682,7 +703,7 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
       const int u = (tid + NT * k) % (NT * UPT / 2);
       const int c = u % CPR;
       const int r = u / CPR;  // token row of the chunk
-      u32x4 v = stg[slot][k];
+      u32x4 v = widen_stage(stg[slot][k]);
       if (!plain) {
         if (tb + r >= t_end) v = u32x4{0u, 0u, 0u, 0u};
         else if (stg_bad[slot]) v = is_k ? u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}
@@ -809,7 +830,7 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
         for (int qq = 0; qq < 4; ++qq)
           store_bf16x4(dst + 32 * db + 8 * qq,
                        f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2],
-                             o[db][4 * qq + 3]} * inv);
+                             o[db][4 * qq + 3]} * (inv * v_scale));
     }
   } else {
     const size_t slot = orow * num_splits + s;
@@ -818,7 +839,8 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
         *reinterpret_cast<f32x4*>(ws_acc + slot * D + 32 * db + 8 * qq + 4 * g) =
-            f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
+            f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]} *
+            v_scale;
     if (g == 0) *reinterpret_cast<float2*>(ws_ml + slot * 2) = make_float2(m_run, l_tot);
   }
 }
@@ -862,7 +884,7 @@ __global__ __launch_bounds__(256) void mq_reduce_kernel(
   store_bf16x4(out + (size_t)row * D + d4, res);
 }
 
-template <int D, int RT>
+template <int D, int RT, bool kFp8>
 int launch_mq_drt(const MqLaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int gqa = a.num_q_heads / a.num_kv_heads;
@@ -873,11 +895,13 @@ int launch_mq_drt(const MqLaunchArgs& a) {
                   (void*)&a.batch,       (void*)&a.num_tokens,    (void*)&a.num_kv_heads,
                   (void*)&gqa,           (void*)&a.max_pages,     (void*)&a.num_pages,
                   (void*)&a.max_query_len, (void*)&a.row_blocks,  (void*)&a.split_pages,
-                  (void*)&a.num_splits,  (void*)&a.score_scale,   (void*)&a.order_by_work};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq_kernel<D, RT>), grid,
+                  (void*)&a.num_splits,  (void*)&a.score_scale,   (void*)&a.v_scale,
+                  (void*)&a.order_by_work};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq_kernel<D, RT, kFp8>), grid,
                               dim3(64 * mq_waves(D, RT)), args, mq_lds_bytes(D, RT), stream);
 }
 
+template <bool kFp8>
 int launch_mq32(const MqLaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int gqa = a.num_q_heads / a.num_kv_heads;
@@ -888,22 +912,23 @@ int launch_mq32(const MqLaunchArgs& a) {
                   (void*)&a.batch,       (void*)&a.num_tokens,    (void*)&a.num_kv_heads,
                   (void*)&gqa,           (void*)&a.max_pages,     (void*)&a.num_pages,
                   (void*)&a.max_query_len, (void*)&a.row_blocks,  (void*)&a.split_pages,
-                  (void*)&a.num_splits,  (void*)&a.score_scale,   (void*)&a.order_by_work};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq32_kernel), grid,
+                  (void*)&a.num_splits,  (void*)&a.score_scale,   (void*)&a.v_scale,
+                  (void*)&a.order_by_work};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq32_kernel<kFp8>), grid,
                               dim3(kM32Threads), args, mq32_lds_bytes(), stream);
 }
 
-template <int D>
+template <int D, bool kFp8>
 int launch_mq_d(const MqLaunchArgs& a) {
   switch (a.row_tiles) {
     case 1:
-      if constexpr (D == 128) return launch_mq_drt<128, 1>(a);
+      if constexpr (D == 128) return launch_mq_drt<128, 1, kFp8>(a);
       else return -1;  // head_dim 256 plans start at 2 row tiles
-    case 2: return launch_mq_drt<D, 2>(a);
-    case 4: return launch_mq_drt<D, 4>(a);
+    case 2: return launch_mq_drt<D, 2, kFp8>(a);
+    case 4: return launch_mq_drt<D, 4, kFp8>(a);
     default:
-      if constexpr (D == 128) return launch_mq32(a);
-      else return launch_mq_drt<D, 8>(a);
+      if constexpr (D == 128) return launch_mq32<kFp8>(a);
+      else return launch_mq_drt<D, 8, kFp8>(a);
   }
 }
 
@@ -933,7 +958,8 @@ int mq_row_tiles(int rows_per_head, int head_dim) {
 }
 
 int launch_mq(const MqLaunchArgs& a) {
-  return a.head_dim == 128 ? launch_mq_d<128>(a) : launch_mq_d<256>(a);
+  if (a.kv_fp8) return a.head_dim == 128 ? launch_mq_d<128, true>(a) : launch_mq_d<256, true>(a);
+  return a.head_dim == 128 ? launch_mq_d<128, false>(a) : launch_mq_d<256, false>(a);
 }
 
 int launch_mq_reduce(const MqLaunchArgs& a) {

@@ -8,8 +8,8 @@ the library is missing, importing the binding raises instead of falling back.
 
 Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_plan``,
 ``pa_workspace_size``, ``pa_decode_partials``, ``pa_merge_partials``,
-``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_attention_prologue``,
-``pa_status_string``, ``pa_abi_version``.
+``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_mq_attention_fp8``,
+``pa_attention_prologue``, ``pa_status_string``, ``pa_abi_version``.
 """
 
 from __future__ import annotations
@@ -147,6 +147,12 @@ def _load():
         ctypes.POINTER(PaMqShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    lib.pa_mq_attention_fp8.restype = ctypes.c_int
+    lib.pa_mq_attention_fp8.argtypes = [
+        ctypes.POINTER(PaMqShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
     ]
     lib.pa_attention_prologue.restype = ctypes.c_int
     lib.pa_attention_prologue.argtypes = [
@@ -390,19 +396,8 @@ def pa_mq_plan(shape: PaMqShape) -> PaPlan:
     return plan
 
 
-def pa_mq_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                    block_table: torch.Tensor, context_lens: torch.Tensor,
-                    query_start: torch.Tensor, max_query_len: int,
-                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                    split_pages: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Causal multi-query attention over a paged BF16 cache; returns ``out`` [T, Hq, D].
-
-    q [T, Hq, D] bf16 packs the query tokens of all sequences token-major;
-    sequence b owns rows query_start[b] .. query_start[b+1]-1 (query_start
-    [B+1] int32 on the GPU), which are the last tokens of its context_lens[b]
-    cached tokens. ``max_query_len`` bounds every sequence's row count (a host
-    integer, as the launch is sized from it).
-    """
+def _mq(q, k_cache, v_cache, block_table, context_lens, query_start, max_query_len, scale,
+        out, split_pages, workspace, fp8, k_scale, v_scale):
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("expected q [T,Hq,D] and k_cache == v_cache shape [N,P,Hkv,D]")
     T, Hq, D = q.shape
@@ -411,8 +406,9 @@ def pa_mq_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     B = block_table.shape[0] if block_table.dim() == 2 else -1
     if B < 0 or context_lens.shape != (B,) or query_start.shape != (B + 1,):
         raise ValueError("expected block_table [B, W], context_lens [B], query_start [B+1]")
-    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, torch.bfloat16),
-                        ("v_cache", v_cache, torch.bfloat16),
+    kv = torch.uint8 if fp8 else torch.bfloat16
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, kv),
+                        ("v_cache", v_cache, kv),
                         ("block_table", block_table, torch.int32),
                         ("context_lens", context_lens, torch.int32),
                         ("query_start", query_start, torch.int32)):
@@ -433,13 +429,53 @@ def pa_mq_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         workspace = _workspace(q.device, plan.workspace_bytes)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.pa_mq_attention(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
-                              v_cache.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
-                              query_start.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
-                              ws_ptr, ws_bytes, _stream(q.device))
+    if fp8:
+        st = _lib.pa_mq_attention_fp8(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
+                                      v_cache.data_ptr(), ctypes.c_float(k_scale),
+                                      ctypes.c_float(v_scale), block_table.data_ptr(),
+                                      context_lens.data_ptr(), query_start.data_ptr(),
+                                      ctypes.c_float(scale), out.data_ptr(), ws_ptr, ws_bytes,
+                                      _stream(q.device))
+        name = "pa_mq_attention_fp8"
+    else:
+        st = _lib.pa_mq_attention(ctypes.byref(shape), q.data_ptr(), k_cache.data_ptr(),
+                                  v_cache.data_ptr(), block_table.data_ptr(),
+                                  context_lens.data_ptr(), query_start.data_ptr(),
+                                  ctypes.c_float(scale), out.data_ptr(), ws_ptr, ws_bytes,
+                                  _stream(q.device))
+        name = "pa_mq_attention"
     if st != PA_OK:
-        raise PagedAttnError(st, "pa_mq_attention")
+        raise PagedAttnError(st, name)
     return out
+
+
+def pa_mq_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_table: torch.Tensor, context_lens: torch.Tensor,
+                    query_start: torch.Tensor, max_query_len: int,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    split_pages: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal multi-query attention over a paged BF16 cache; returns ``out`` [T, Hq, D].
+
+    q [T, Hq, D] bf16 packs the query tokens of all sequences token-major;
+    sequence b owns rows query_start[b] .. query_start[b+1]-1 (query_start
+    [B+1] int32 on the GPU), which are the last tokens of its context_lens[b]
+    cached tokens. ``max_query_len`` bounds every sequence's row count (a host
+    integer, as the launch is sized from it).
+    """
+    return _mq(q, k_cache, v_cache, block_table, context_lens, query_start, max_query_len,
+               scale, out, split_pages, workspace, False, 1.0, 1.0)
+
+
+def pa_mq_attention_fp8(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                        k_scale: float, v_scale: float, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, query_start: torch.Tensor,
+                        max_query_len: int, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None, split_pages: int = 0,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``pa_mq_attention`` over FP8-E4M3 pools (uint8 codes [N, 128, Hkv, D])
+    with per-tensor scales: values are code * k_scale and code * v_scale."""
+    return _mq(q, k_codes, v_codes, block_table, context_lens, query_start, max_query_len,
+               scale, out, split_pages, workspace, True, k_scale, v_scale)
 
 
 def pa_attention_prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == ["pa_abi_version", "pa_attention_prologue", "pa_decode", "pa_decode_fp8",
                      "pa_decode_partials", "pa_kv_write", "pa_merge_partials", "pa_mq_attention",
-                     "pa_mq_plan", "pa_plan", "pa_status_string", "pa_workspace_size"]
+                     "pa_mq_attention_fp8", "pa_mq_plan", "pa_plan", "pa_status_string",
+                     "pa_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -305,6 +306,35 @@ def test_mq_rejects_bad_pointers():
     a = list(ok)
     a[9] = plan.workspace_bytes - 1
     assert pa.lib.pa_mq_attention(ctypes.byref(s), *a) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+
+
+@fake_pointers
+def test_mq_fp8_rejects_bad_arguments():
+    # the FP8 entry point runs the same checks, plus finite k_scale and v_scale
+    d = 1 << 20
+    s = _mq()
+    plan = pa.pa_mq_plan(s)
+    f = ctypes.c_float
+    ok = [d, d, d, f(0.5), f(0.25), d, d, d, f(0.1), d, d, plan.workspace_bytes, None]
+    assert pa.lib.pa_mq_attention_fp8(None, *ok) == pa.PA_ERR_NULL_POINTER
+    for i in (3, 4, 8):
+        for bad in (float("nan"), float("inf")):
+            a = list(ok)
+            a[i] = f(bad)
+            assert pa.lib.pa_mq_attention_fp8(ctypes.byref(s), *a) == \
+                pa.PA_ERR_INVALID_ARGUMENT, (i, bad)
+    for i in (0, 1, 2, 5, 6, 7, 9, 10):
+        a = list(ok)
+        a[i] = None
+        assert pa.lib.pa_mq_attention_fp8(ctypes.byref(s), *a) == pa.PA_ERR_NULL_POINTER, i
+    a = list(ok)
+    a[1] = d + 8
+    assert pa.lib.pa_mq_attention_fp8(ctypes.byref(s), *a) == pa.PA_ERR_INVALID_ARGUMENT
+    a = list(ok)
+    a[11] = plan.workspace_bytes - 1
+    assert pa.lib.pa_mq_attention_fp8(ctypes.byref(s), *a) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    s.head_dim = 64
+    assert pa.lib.pa_mq_attention_fp8(ctypes.byref(s), *ok) == pa.PA_ERR_UNSUPPORTED
 
 
 # ---- attention prologue ----------------------------------------------------------

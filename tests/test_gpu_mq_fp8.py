@@ -1,0 +1,130 @@
+"""GPU parity of causal multi-query attention over FP8-E4M3 pools
+(pa_mq_attention_fp8) against the FP64 oracle, and its agreement with the
+BF16 path when the BF16 cache holds exactly the FP8 values."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import announce, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    from paged_gqa_attention_amd import pagedattn  # noqa: F401
+
+
+def run_fp8(w, f, split_pages=0, k_scale=None, v_scale=None):
+    from paged_gqa_attention_amd import pagedattn as pa
+    out = pa.pa_mq_attention_fp8(w.q.to(DEV), f.k_codes.to(DEV), f.v_codes.to(DEV),
+                                 f.k_scale if k_scale is None else k_scale,
+                                 f.v_scale if v_scale is None else v_scale,
+                                 w.block_table.to(DEV), w.context_lens.to(DEV),
+                                 w.query_start.to(DEV), w.max_query_len, scale=w.scale,
+                                 split_pages=split_pages)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def oracle_fp8(w, f):
+    return oracle.paged_multi_query_attention_fp8(w.q, f.k_codes, f.v_codes, f.k_scale, f.v_scale,
+                                                  w.block_table, w.context_lens, w.query_start,
+                                                  w.scale)
+
+
+def oracle_fp8_rows(w, f, tokens):
+    """Selected packed rows one at a time: row i of a chunk of Lq rows is
+    single-query FP8 decode over the first ctx - Lq + i + 1 tokens."""
+    qs = w.query_start.tolist()
+    res = []
+    for t in tokens:
+        b = max(i for i in range(len(qs) - 1) if qs[i] <= t < qs[i + 1])
+        n = int(w.context_lens[b]) - (qs[b + 1] - qs[b]) + (t - qs[b]) + 1
+        res.append(oracle.paged_decode_attention_fp8(
+            w.q[t:t + 1], f.k_codes, f.v_codes, f.k_scale, f.v_scale, w.block_table[b:b + 1],
+            torch.tensor([max(n, 0)], dtype=torch.int32), w.scale)[0])
+    return np.stack(res)
+
+
+@pytest.mark.parametrize("split_pages", [0, 1, 3])
+def test_small_mixed_chunks_and_splits(split_pages):
+    announce(f"mq fp8 small mixed sp{split_pages}")
+    w = workloads.build_mq([4, 1, 7, 40], [9, 128, 300, 650], 40, 8, 128, seed=11, max_pages=6,
+                           pool="packed")
+    f = workloads.quantize_fp8(w)
+    assert_parity(run_fp8(w, f, split_pages), oracle_fp8(w, f), f"mq fp8 sp{split_pages}")
+
+
+def test_mtp4_full_size():
+    w = workloads.mq_config("mtp4")
+    announce("mq fp8 mtp4 full size")
+    f = workloads.quantize_fp8(w)
+    assert_parity(run_fp8(w, f), oracle_fp8(w, f), "mq fp8 mtp4")
+
+
+@pytest.mark.parametrize("name", ["prefill512", "wide257"])
+def test_prefill_full_size_sampled_rows(name):
+    w = workloads.mq_config(name)
+    announce(f"mq fp8 {name} full size")
+    f = workloads.quantize_fp8(w)
+    out = run_fp8(w, f)
+    assert torch.isfinite(out.float()).all()
+    gen = torch.Generator().manual_seed(6)
+    qs = w.query_start.tolist()
+    toks = sorted(set([qs[b] for b in range(len(qs) - 1)] + [qs[b + 1] - 1 for b in range(len(qs) - 1)]
+                      + torch.randint(0, w.num_tokens, (16,), generator=gen).tolist()))
+    assert_parity(out[toks], oracle_fp8_rows(w, f, toks), f"mq fp8 {name} sampled")
+
+
+@pytest.mark.parametrize("lqs,D,Hq,Hkv", [([1, 3], 256, 16, 2), ([257], 256, 16, 2),
+                                          ([2, 30], 128, 16, 16)])
+def test_head_shapes(lqs, D, Hq, Hkv):
+    announce(f"mq fp8 {Hq}/{Hkv}/{D} lq={lqs}")
+    ctx = [c + l for c, l in zip([700, 90], lqs)][: len(lqs)]
+    w = workloads.build_mq(lqs, ctx, Hq, Hkv, D, seed=len(lqs) + D, max_pages=8, pool="packed")
+    f = workloads.quantize_fp8(w)
+    assert_parity(run_fp8(w, f), oracle_fp8(w, f), f"mq fp8 {Hq}/{Hkv}/{D}")
+
+
+@pytest.mark.parametrize("lqs", [[4, 6], [40, 33]])
+def test_same_bits_as_bf16_path_on_exact_values(lqs):
+    # with unit scales and a BF16 cache holding exactly the decoded FP8 values
+    # (every E4M3 value is a BF16 value), both entry points stage the same BF16
+    # operands: the outputs must agree bit for bit (both row-tile regimes)
+    from paged_gqa_attention_amd import pagedattn as pa
+    announce(f"mq fp8 vs bf16 bits lq={lqs}")
+    w = workloads.build_mq(lqs, [300, 520], 40, 8, 128, seed=13, max_pages=5, pool="packed")
+    f = workloads.quantize_fp8(w)
+    kb = torch.from_numpy(oracle.decode_fp8_e4m3(f.k_codes.numpy())).to(torch.bfloat16)
+    vb = torch.from_numpy(oracle.decode_fp8_e4m3(f.v_codes.numpy())).to(torch.bfloat16)
+    out8 = run_fp8(w, f, k_scale=1.0, v_scale=1.0)
+    out16 = pa.pa_mq_attention(w.q.to(DEV), kb.to(DEV), vb.to(DEV), w.block_table.to(DEV),
+                               w.context_lens.to(DEV), w.query_start.to(DEV), w.max_query_len,
+                               scale=w.scale).cpu()
+    torch.cuda.synchronize()
+    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+
+
+def test_nan_code_in_a_visible_slot_gives_nan_rows():
+    # a NaN code (0x7F) in K at a slot only the last rows of the chunk see
+    announce("mq fp8 NaN code")
+    w = workloads.build_mq([4], [260], 40, 8, 128, seed=14, max_pages=3, pool="packed")
+    f = workloads.quantize_fp8(w)
+    k = f.k_codes.clone()
+    page = int(w.block_table[0, 2])
+    k[page, 2, 3, 5] = 0x7F           # token 258, KV head 3: seen by rows 2 and 3
+    f2 = workloads.Fp8Pools(k, f.v_codes, f.k_scale, f.v_scale)
+    out = run_fp8(w, f2).float().reshape(4, 8, 5, 128)
+    assert torch.isnan(out[2:, 3]).all()
+    ref = torch.from_numpy(oracle_fp8(w, f)).reshape(4, 8, 5, 128).numpy()
+    keep = np.ones((4, 8), bool)
+    keep[2:, 3] = False
+    assert_parity(out.to(torch.bfloat16)[torch.from_numpy(keep)], ref[keep], "mq fp8 NaN code")

@@ -77,3 +77,30 @@ def test_empty_chunks_and_short_context():
     assert np.all(np.isfinite(out))
     # its last query sees both tokens: a two-token softmax
     assert not np.array_equal(out[2], np.zeros_like(out[2]))
+
+
+def test_fp8_single_query_is_fp8_decode():
+    # FP8 pools: one query per sequence is decode over the same FP8 pools
+    w, q, qs = _packed(5, [1, 1, 1], [7, 129, 260])
+    f = workloads.quantize_fp8(w)
+    a = oracle.paged_multi_query_attention_fp8(q, f.k_codes, f.v_codes, f.k_scale, f.v_scale,
+                                               w.block_table, w.context_lens, qs, w.scale)
+    b = oracle.paged_decode_attention_fp8(q, f.k_codes, f.v_codes, f.k_scale, f.v_scale,
+                                          w.block_table, w.context_lens, w.scale)
+    assert np.array_equal(a, b)
+
+
+def test_fp8_scales_act_linearly():
+    # k_scale enters the logits like the logit scale does; v_scale multiplies
+    # the output. Powers of two keep both exact in FP64.
+    w, q, qs = _packed(6, [3, 5], [40, 300])
+    f = workloads.quantize_fp8(w)
+    bt, ctx = w.block_table, w.context_lens
+    base = oracle.paged_multi_query_attention_fp8(q, f.k_codes, f.v_codes, 0.5, 0.25, bt, ctx,
+                                                  qs, 0.125)
+    k_swap = oracle.paged_multi_query_attention_fp8(q, f.k_codes, f.v_codes, 1.0, 0.25, bt, ctx,
+                                                    qs, 0.0625)
+    v_twice = oracle.paged_multi_query_attention_fp8(q, f.k_codes, f.v_codes, 0.5, 0.5, bt, ctx,
+                                                     qs, 0.125)
+    assert np.allclose(base, k_swap, rtol=1e-13, atol=1e-15)
+    assert np.array_equal(2.0 * base, v_twice)
