@@ -324,6 +324,32 @@ pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* 
                                   float rope_scale, void* q_out, void* k_cache, void* v_cache,
                                   void* stream);
 
+/* A whole decode step's attention in one call: the prologue above for each
+ * sequence's new token, fused into pa_decode's first kernel, as the
+ * "Qwen3-14B" decode_fwd section runs it (the attention kernel's phase 0).
+ * Sequence b's new token is token context_lens[b] - 1 of its context: its raw
+ * q rows (q, BF16 [B, Hq, D], before norm and RoPE), k_new[b] and v_new[b]
+ * (BF16 [B, Hkv, D]) are normalised and rotated at positions[b] exactly as
+ * pa_attention_prologue does (angles: FP64 frequencies, FP64 reduction modulo
+ * 2 pi, FP32 sine and cosine; the rest in FP32, rounded to BF16); K and V go
+ * to slot slot_mapping[b] of the pools (negative or >= N * P: not written),
+ * and attention over tokens [0, context_lens[b]) follows, with the new token's
+ * K and V taken from the fused prologue itself. The slot must be the one the
+ * block table gives token context_lens[b] - 1, and no other sequence of the
+ * call may read it. A sequence with context 0 has no new token: its output
+ * rows are zeros and nothing is written. Shapes, pools (BF16 only), block
+ * table, context lengths, scale, out, workspace and errors are as for
+ * pa_decode; eps, rope_base, rope_scale and the weights as for
+ * pa_attention_prologue; k_new, v_new 16-byte aligned; positions and
+ * slot_mapping INT32 [B]. Saves the prologue's own launch per decode layer. */
+pa_status_t pa_decode_step(const pa_shape_t* shape, const void* q, const void* k_new,
+                           const void* v_new, const void* q_norm_weight,
+                           const void* k_norm_weight, const int32_t* positions,
+                           const int32_t* slot_mapping, float eps, float rope_base,
+                           float rope_scale, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens, float scale,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

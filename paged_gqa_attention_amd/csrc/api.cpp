@@ -248,6 +248,8 @@ pa_status_t prepare(const pa_shape_t* shape, const void* q, const void* k_cache,
   a->score_scale = scale * 1.4426950408889634f;  // natural-exp softmax computed as exp2
   a->v_scale = 1.0f;
   a->kv_fp8 = false;
+  a->decode_step = false;
+  a->step = pa::DecodeStepArgs{};
   a->stream = stream;
   return PA_OK;
 }
@@ -328,6 +330,46 @@ pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cach
   st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, out, workspace,
                workspace_bytes, stream, true, true, &a);
   if (st != PA_OK) return st;
+  if (pa::launch_partition(a) != 0) return PA_ERR_LAUNCH;
+  return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+pa_status_t pa_decode_step(const pa_shape_t* shape, const void* q, const void* k_new,
+                           const void* v_new, const void* q_norm_weight,
+                           const void* k_norm_weight, const int32_t* positions,
+                           const int32_t* slot_mapping, float eps, float rope_base,
+                           float rope_scale, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens, float scale,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->batch == 0) return PA_OK;
+  if (!k_new || !v_new || !q_norm_weight || !k_norm_weight || !positions || !slot_mapping)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q_norm_weight) ||
+      !aligned16(k_norm_weight) || ((uintptr_t)positions & 3u) || ((uintptr_t)slot_mapping & 3u))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(eps) || eps < 0.f || !isfinite(rope_base) || rope_base <= 0.f ||
+      !isfinite(rope_scale) || rope_scale <= 0.f)
+    return PA_ERR_INVALID_ARGUMENT;
+  pa::LaunchArgs a;
+  st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, out, workspace,
+               workspace_bytes, stream, true, true, &a);
+  if (st != PA_OK) return st;
+  const double d = shape->head_dim;
+  a.decode_step = true;
+  a.step.k_new = static_cast<const uint16_t*>(k_new);
+  a.step.v_new = static_cast<const uint16_t*>(v_new);
+  a.step.q_norm_w = static_cast<const uint16_t*>(q_norm_weight);
+  a.step.k_norm_w = static_cast<const uint16_t*>(k_norm_weight);
+  a.step.positions = positions;
+  a.step.slot_mapping = slot_mapping;
+  a.step.k_pool = static_cast<uint16_t*>(k_cache);
+  a.step.v_pool = static_cast<uint16_t*>(v_cache);
+  a.step.num_slots = (long long)shape->num_pages * shape->page_size;
+  a.step.eps = eps;
+  a.step.inv_scale = 1.0 / (double)rope_scale;
+  a.step.log2r = -2.0 * log2((double)rope_base) / d;
   if (pa::launch_partition(a) != 0) return PA_ERR_LAUNCH;
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }

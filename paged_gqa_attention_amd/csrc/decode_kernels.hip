@@ -73,17 +73,107 @@ __host__ __device__ constexpr int wave_tile_words(int split_tokens) {
   return split_tokens * HeadPad<G>::value;
 }
 
+// 2 pi as a double plus the remainder, for reducing rotation angles.
+constexpr double k2PiHi = 6.283185307179586;
+constexpr double k2PiLo = 2.4492935982947064e-16;
+constexpr double kInv2Pi = 0.15915494309189535;
+
+// Per-head RMSNorm and NeoX RoPE ("Qwen 3", TensorSharp docs, sections 3 and
+// 4.1: each head normalised on its own with head_dim weights, then dim i
+// rotated with dim i + D/2 by theta_i = pos * base^(-2i/D) / scale) of a
+// head vector held in the score MFMA's operand layout: lane (lq, lr) holds
+// dims 32*kk + 8*lq + j (kk < D/32, j < 8) of row lr, so a dim's partner
+// d + D/2 is the same lane's k-step kk + D/64 and the sum of squares needs
+// only the 4 lanes of the row. Each frequency base^(-2i/D) / scale is taken
+// in FP64 as 2^(i * log2(r)) with log2(r) = -2 log2(base) / D (at position
+// 2^27 the angle is still right to ~1e-6), each angle is reduced modulo 2 pi
+// in FP64, and its sine and cosine taken in FP32. Norm and rotation run in FP32 and round to BF16
+// (nearest even), like the separate prologue kernel.
+template <int D>
+struct Rope {
+  static constexpr int KK = D / 32;
+  static constexpr int KH = KK / 2;
+  static constexpr int NA = D / 128;  // angles per lane
+  float c_own[NA];  // cos and sin of angles i = lane + 64 a
+  float s_own[NA];
+
+  __device__ __forceinline__ Rope(int pos, int lane, double inv_scale, double log2r) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const double f = inv_scale * exp2((double)(lane + 64 * a) * log2r);
+      const double th = (double)pos * f;
+      const double n = rint(th * kInv2Pi);
+      double red = fma(-n, k2PiHi, th);
+      red = fma(-n, k2PiLo, red);
+      sincosf((float)red, &s_own[a], &c_own[a]);
+    }
+  }
+
+  // w points at the weights of the lane's dims 8*lq (BF16 [D], 16-byte aligned)
+  __device__ __forceinline__ void norm_rotate(u32x4 (&x)[KK], const uint16_t* w, float eps,
+                                              int lq) const {
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bf16_lo(x[kk][i]);
+        const float b = bf16_hi(x[kk][i]);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+    for (int m = 0; m < KH; ++m) {
+      const u32x4 wl = load16(w + 32 * m);
+      const u32x4 wh = load16(w + 32 * (m + KH));
+      u32x4 lo_out, hi_out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float o[2][2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          // the lane's dim pair (32m + 8lq + 2i + e, + D/2): angle index = the
+          // first dim, held by lane 32*(m%2) + 8lq + 2i + e (times 64 m/2)
+          const int src = 32 * (m % 2) + 8 * lq + 2 * i + e;
+          const float cs = __shfl(c_own[m / 2], src);
+          const float sn = __shfl(s_own[m / 2], src);
+          const float xl = e ? bf16_hi(x[m][i]) : bf16_lo(x[m][i]);
+          const float xh = e ? bf16_hi(x[m + KH][i]) : bf16_lo(x[m + KH][i]);
+          const float yl = xl * rinv * (e ? bf16_hi(wl[i]) : bf16_lo(wl[i]));
+          const float yh = xh * rinv * (e ? bf16_hi(wh[i]) : bf16_lo(wh[i]));
+          o[0][e] = yl * cs - yh * sn;
+          o[1][e] = yh * cs + yl * sn;
+        }
+        lo_out[i] = (uint32_t)f32_to_bf16(o[0][0]) | ((uint32_t)f32_to_bf16(o[0][1]) << 16);
+        hi_out[i] = (uint32_t)f32_to_bf16(o[1][0]) | ((uint32_t)f32_to_bf16(o[1][1]) << 16);
+      }
+      x[m] = lo_out;
+      x[m + KH] = hi_out;
+    }
+  }
+};
+
 // kFp8: the K/V pools hold FP8 E4M3 codes (one byte per value) with
 // per-tensor scales; k_scale is folded into score_scale on the host and
 // v_scale multiplies the split's output sums. Otherwise they hold BF16.
-template <int D, int G, bool kFp8>
+// kStep (BF16 pools): the attention prologue of a decode step runs here too.
+// q arrives before RMSNorm and RoPE; every wave normalises and rotates its
+// G query heads itself, and the wave whose split holds the new token (token
+// ctx - 1) normalises and rotates the new K row, writes K and V to the pools
+// at the token's slot, and uses both from registers in its own tiles.
+template <int D, int G, bool kFp8, bool kStep>
 __global__ __launch_bounds__(kThreads) void partition_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, int batch, int num_kv_heads, int heads_per_wg, int max_pages,
-    int num_pages, int split_tokens, int num_splits, float score_scale, float v_scale) {
+    int num_pages, int split_tokens, int num_splits, float score_scale, float v_scale,
+    DecodeStepArgs step) {
   static_assert(D == 128 || D == 256, "head_dim");
+  static_assert(!(kStep && kFp8), "the fused prologue writes BF16 pools");
   static_assert(G >= 1 && G <= 16, "gqa ratio");
   constexpr int ESZ = kFp8 ? 1 : 2;       // bytes per cached K/V value
   constexpr int GP = HeadPad<G>::value;   // LDS row stride (floats)
@@ -99,6 +189,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   static_assert(16 % BR == 0, "P.V blocks must tile the 16-token score tiles");
 
   extern __shared__ float smem[];
+  using VChunk4 = u32x4;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -156,10 +247,52 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     }
   }
   int ctx = context_lens[b];
+  int pos = 0;
+  if constexpr (kStep) pos = step.positions[b];
   ctx = ctx < 0 ? 0 : (ctx > max_pages * kPage ? max_pages * kPage : ctx);
   const int n_s = min(ctx - t0, split_tokens);
   if (n_s <= 0) return;  // split past the context: nothing to write (no barriers below)
   page_id = (unsigned)page_id < (unsigned)num_pages ? page_id : -1;  // outside the pool: -1
+
+  // ---- fused prologue (kStep) -------------------------------------------
+  // tnew: the new token's index in this split, or -1 if another split has it.
+  // Its K row, V chunk and slot load here; the norm and rotation run once the
+  // first K tile's loads are out (the pipeline's ready hook below).
+  int tnew = -1;
+  u32x4 knew[KK];  // new K row in the score MFMA's operand layout (rotated)
+  VChunk4 vnew;    // this lane's 16 bytes of the new V row (dims 8*(lane % (D/8)))
+  long long slot = -1;
+  if constexpr (kStep) {
+    tnew = ctx - 1 - t0 < split_tokens ? ctx - 1 - t0 : -1;
+    if (tnew >= 0) {
+      const size_t row = (size_t)b * num_kv_heads + h;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) knew[kk] = load16(step.k_new + row * D + 32 * kk + 8 * lq);
+      vnew = load16(step.v_new + row * D + 8 * (lane % (D / 8)));
+      slot = step.slot_mapping[b];
+    }
+  }
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (kStep) {
+      const Rope<D> rope(pos, lane, step.inv_scale, step.log2r);
+      rope.norm_rotate(qa, step.q_norm_w + 8 * lq, step.eps, lq);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        if (lr >= G) qa[kk] = u32x4{0u, 0u, 0u, 0u};  // padded rows stay zero
+      if (tnew >= 0) {
+        rope.norm_rotate(knew, step.k_norm_w + 8 * lq, step.eps, lq);
+        if (slot >= 0 && slot < step.num_slots) {
+          const size_t dst = ((size_t)slot * num_kv_heads + h) * D;
+          if (lr == 0) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+              *reinterpret_cast<u32x4*>(step.k_pool + dst + 32 * kk + 8 * lq) = knew[kk];
+          }
+          if (lane < D / 8) *reinterpret_cast<u32x4*>(step.v_pool + dst + 8 * lane) = vnew;
+        }
+      }
+    }
+  };
 
   const size_t page_bytes = (size_t)kPage * num_kv_heads * D * ESZ;
   const uint32_t row_bytes = (uint32_t)num_kv_heads * D * ESZ;  // token stride
@@ -192,6 +325,9 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   auto score_tile = [&](int tile, const u32x4 (&buf)[KL], bool bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // the new token's row comes from registers (the pool may still hold the
+    // old contents of its slot when this tile was loaded)
+    const bool new_row = kStep && tnew >= tl && tnew < tl + 16 && lr == tnew - tl;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 kb;
@@ -199,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
         const u32x4 w = buf[kk >> 1];
         kb = (kk & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
       } else {
-        kb = buf[kk];
+        kb = new_row ? knew[kk] : buf[kk];
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
                                                     __builtin_bit_cast(bf16x8, kb), acc, 0, 0, 0);
@@ -222,8 +358,9 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     u32x4 kbuf[KNB][KL];
     bool kbad[KNB];
     pipeline<KNB>(
-        ntile, [&](int i, int slot) __attribute__((always_inline)) { load_k(i, kbuf[slot], kbad[slot]); },
-        [&](int i, int slot) __attribute__((always_inline)) { score_tile(i, kbuf[slot], kbad[slot]); });
+        ntile, [&](int i, int sl) __attribute__((always_inline)) { load_k(i, kbuf[sl], kbad[sl]); },
+        [&](int i, int sl) __attribute__((always_inline)) { score_tile(i, kbuf[sl], kbad[sl]); },
+        prologue);
   }
 
   // ---- V loads of the first P.V step go out before the softmax ------------
@@ -321,6 +458,13 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
       for (int u = 0; u < PV_U; ++u)
         if (tl + u * RPI + r >= n_s) buf[u] = VChunk{};
     }
+    if constexpr (kStep) {  // the new token's V row from registers
+      if (tnew >= tl && tnew < tl + BR) {
+#pragma unroll
+        for (int u = 0; u < PV_U; ++u)
+          if (tl + u * RPI + r == tnew) buf[u] = vnew;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < PV_U; ++u) {
       const int t = tl + u * RPI + r;
@@ -417,7 +561,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
   store_bf16x4(out + (size_t)row * D + d4, res);
 }
 
-template <int D, int G, bool kFp8>
+template <int D, int G, bool kFp8, bool kStep>
 int launch_partition_dgt(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int hpw = heads_per_workgroup(a.num_kv_heads);
@@ -428,14 +572,16 @@ int launch_partition_dgt(const LaunchArgs& a) {
                   (void*)&a.ws_ml,       (void*)&a.batch,        (void*)&a.num_kv_heads,
                   (void*)&hpw,           (void*)&a.max_pages,    (void*)&a.num_pages,
                   (void*)&a.split_tokens, (void*)&a.num_splits,   (void*)&a.score_scale,
-                  (void*)&a.v_scale};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G, kFp8>),
+                  (void*)&a.v_scale,     (void*)&a.step};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<D, G, kFp8, kStep>),
                               grid, dim3(kThreads), args, lds, stream);
 }
 
 template <int D, int G>
 int launch_partition_dg(const LaunchArgs& a) {
-  return a.kv_fp8 ? launch_partition_dgt<D, G, true>(a) : launch_partition_dgt<D, G, false>(a);
+  if (a.kv_fp8) return launch_partition_dgt<D, G, true, false>(a);
+  if (a.decode_step) return launch_partition_dgt<D, G, false, true>(a);
+  return launch_partition_dgt<D, G, false, false>(a);
 }
 
 template <int D>

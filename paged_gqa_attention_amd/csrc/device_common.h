@@ -71,12 +71,15 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // unconditionally: if some path could enter the loop with fewer loads in
 // flight, the compiler would have to assume the youngest loads are the ones
 // being used and wait for all of them, collapsing the pipeline to depth 1.
-template <int NB, class Load, class Use>
-__device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
+// `ready` runs once after the first NB-1 loads are issued and before the
+// first use: work the uses depend on overlaps those loads' latency.
+template <int NB, class Load, class Use, class Ready>
+__device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use, Ready&& ready) {
   int j = 0;
   if (n > 2 * NB - 2) {
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) load(i, i);
+    ready();
     for (; j + 2 * NB - 2 < n; j += NB) {
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
@@ -89,6 +92,7 @@ __device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
       if (i < n) load(i, i);
+    ready();
   }
 #pragma unroll
   for (int u = 0; u < 2 * NB - 2; ++u) {
@@ -97,6 +101,11 @@ __device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
       use(j + u, u % NB);
     }
   }
+}
+
+template <int NB, class Load, class Use>
+__device__ __forceinline__ void pipeline(int n, Load&& load, Use&& use) {
+  pipeline<NB>(n, load, use, [] {});
 }
 
 // Log-sum-exp merge of the first nv split partials of one (sequence, query

@@ -7,6 +7,24 @@
 
 namespace pa {
 
+// The attention prologue fused into decode (pa_decode_step): per-head RMSNorm
+// and NeoX RoPE of q and of the step's new K row, and the new token's K/V
+// write, done by the partition kernel itself.
+struct DecodeStepArgs {
+  const uint16_t* k_new;      // bf16 [B, Hkv, D]: the new token's K before norm and RoPE
+  const uint16_t* v_new;      // bf16 [B, Hkv, D]
+  const uint16_t* q_norm_w;   // bf16 [D]
+  const uint16_t* k_norm_w;   // bf16 [D]
+  const int32_t* positions;   // int32 [B]: RoPE position of the new token
+  const int32_t* slot_mapping;// int32 [B]: pool slot of the new token; outside the pool: not written
+  uint16_t* k_pool;           // bf16 [N, P, Hkv, D], written at the new token's slot
+  uint16_t* v_pool;
+  long long num_slots;        // N * P
+  float eps;                  // RMSNorm epsilon
+  double inv_scale;           // 1 / rope_scale
+  double log2r;               // -2 * log2(rope_base) / D
+};
+
 // Everything the two kernels need for one call, already validated on the host.
 struct LaunchArgs {
   const uint16_t* q;          // bf16 [B, Hq, D]
@@ -22,6 +40,8 @@ struct LaunchArgs {
   float score_scale;          // scale * log2(e) (* k_scale for FP8), applied to q.k in FP32
   float v_scale;              // FP8 pools: multiplies the split's output sums
   bool kv_fp8;                // the pools hold FP8 E4M3 codes
+  bool decode_step;           // run the fused prologue (BF16 pools only)
+  DecodeStepArgs step;        // used when decode_step
   void* stream;               // hipStream_t
 };
 

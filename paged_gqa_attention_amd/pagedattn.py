@@ -6,7 +6,7 @@ ABI declared in ``include/pagedattn.h`` through ctypes, on torch's current
 stream. Every step of the computation runs in the library's HIP kernels; if
 the library is missing, importing the binding raises instead of falling back.
 
-Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_plan``,
+Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_decode_step``, ``pa_plan``,
 ``pa_workspace_size``, ``pa_decode_partials``, ``pa_merge_partials``,
 ``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_mq_attention_fp8``,
 ``pa_attention_prologue``, ``pa_status_string``, ``pa_abi_version``.
@@ -161,6 +161,14 @@ def _load():
         ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p,
     ]
+    lib.pa_decode_step.restype = ctypes.c_int
+    lib.pa_decode_step.argtypes = [
+        ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p,
+    ]
     return lib
 
 
@@ -276,6 +284,60 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                         workspace.numel() * workspace.element_size(), _stream(q.device))
     if st != PA_OK:
         raise PagedAttnError(st, "pa_decode")
+    return out
+
+
+def pa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                   positions: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   context_lens: torch.Tensor, scale: Optional[float] = None,
+                   eps: float = 1e-6, rope_base: float = 1e6, rope_scale: float = 1.0,
+                   out: Optional[torch.Tensor] = None, split_pages: int = 0,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A decode step's attention with its prologue fused in; returns ``out``.
+
+    q [B, Hq, D] is the projection's q (before QK-norm and RoPE); k_new and
+    v_new [B, Hkv, D] the new token's K and V; sequence b's new token is token
+    context_lens[b] - 1, rotated at positions[b] and written to
+    slot_mapping[b] of the pools (updated in place), then decode attention over
+    the context follows. Other arguments as for ``pa_decode`` and
+    ``pa_attention_prologue``.
+    """
+    _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    for name, t, shp, dt in (("k_new", k_new, (B, Hkv, D), torch.bfloat16),
+                             ("v_new", v_new, (B, Hkv, D), torch.bfloat16),
+                             ("q_norm_weight", q_norm_weight, (D,), torch.bfloat16),
+                             ("k_norm_weight", k_norm_weight, (D,), torch.bfloat16),
+                             ("positions", positions, (B,), torch.int32),
+                             ("slot_mapping", slot_mapping, (B,), torch.int32)):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}")
+        if t.dtype != dt or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous {dt} on the GPU of q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    shape = shape_of(q, k_cache, block_table, split_pages)
+    if shape.batch == 0:
+        return out
+    need = pa_workspace_size(shape)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    st = _lib.pa_decode_step(ctypes.byref(shape), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                             q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+                             positions.data_ptr(), slot_mapping.data_ptr(), ctypes.c_float(eps),
+                             ctypes.c_float(rope_base), ctypes.c_float(rope_scale),
+                             k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                             context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream(q.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_decode_step")
     return out
 
 

@@ -34,7 +34,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == ["pa_abi_version", "pa_attention_prologue", "pa_decode", "pa_decode_fp8",
-                     "pa_decode_partials", "pa_kv_write", "pa_merge_partials", "pa_mq_attention",
+                     "pa_decode_partials", "pa_decode_step", "pa_kv_write", "pa_merge_partials", "pa_mq_attention",
                      "pa_mq_attention_fp8", "pa_mq_plan", "pa_plan", "pa_status_string",
                      "pa_workspace_size"]
 
@@ -372,3 +372,33 @@ def test_prologue_rejects_bad_arguments():
     s = good()
     s.num_tokens = 0
     assert call(s, [None] * 7 + ok[7:10] + [None, None, None, None]) == pa.PA_OK
+
+
+@fake_pointers
+def test_decode_step_rejects_bad_arguments():
+    # pa_decode_step: pa_decode's checks plus the prologue's parameters
+    d = 1 << 20
+    s = pa.make_shape(2, 40, 8, 128, 32, 64)
+    need = pa.pa_workspace_size(s)
+    f = ctypes.c_float
+    ok = [d, d, d, d, d, d, d, f(1e-6), f(1e6), f(1.0), d, d, d, d, f(0.1), d, d, need, None]
+    call = lambda a: pa.lib.pa_decode_step(ctypes.byref(s), *a)
+    for i in (1, 2, 3, 4, 5, 6):        # k_new .. slot_mapping
+        a = list(ok)
+        a[i] = None
+        assert call(a) == pa.PA_ERR_NULL_POINTER, i
+    for i, bad in ((1, d + 8), (2, d + 4), (3, d + 2), (4, d + 8), (5, d + 2), (6, d + 1)):
+        a = list(ok)
+        a[i] = bad
+        assert call(a) == pa.PA_ERR_INVALID_ARGUMENT, i
+    for i, bad in ((7, -1e-6), (7, float("nan")), (8, 0.0), (8, -2.0), (8, float("inf")),
+                   (9, 0.0), (9, float("nan")), (14, float("inf"))):
+        a = list(ok)
+        a[i] = f(bad)
+        assert call(a) == pa.PA_ERR_INVALID_ARGUMENT, (i, bad)
+    a = list(ok)
+    a[17] = need - 1
+    assert call(a) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    s0 = pa.make_shape(0, 40, 8, 128, 32, 64)
+    assert pa.lib.pa_decode_step(ctypes.byref(s0), *([None] * 7 + ok[7:10] + [None] * 4 +
+                                                     [ok[14], None, None, 0, None])) == pa.PA_OK
