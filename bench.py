@@ -480,6 +480,57 @@ def main():
             }
             print(f"[bench] prologue T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
             del qx, kx, vx, kcx, vcx, qox
+
+        # a whole decode step's attention (pa_decode_step: prologue fused into
+        # decode) on workload 3's shape, against pa_attention_prologue followed
+        # by pa_decode; cold rotation over 8 caches
+        w3 = workloads.config(3)
+        B, Hq, D = w3.q.shape
+        Hkv = w3.k_cache.shape[2]
+        gen = torch.Generator(device=dev).manual_seed(77)
+        bfd = lambda *sz: torch.randn(*sz, device=dev, generator=gen).to(torch.bfloat16)
+        qx, kn, vn, wq, wk = bfd(B, Hq, D), bfd(B, Hkv, D), bfd(B, Hkv, D), bfd(D), bfd(D)
+        btx, ctxx = w3.block_table.to(dev), w3.context_lens.to(dev)
+        ctxl = w3.context_lens.tolist()
+        slx = torch.tensor([int(w3.block_table[b, (c - 1) // 128]) * 128 + (c - 1) % 128
+                            for b, c in enumerate(ctxl)], dtype=torch.int32, device=dev)
+        posx = (ctxx - 1).to(torch.int32)
+        shp = pa.shape_of(w3.q, w3.k_cache, w3.block_table)
+        wsx = torch.empty(pa.pa_workspace_size(shp), dtype=torch.uint8, device=dev)
+        ox, qox = torch.empty_like(qx), torch.empty_like(qx)
+        pools = [(bfd(*w3.k_cache.shape), bfd(*w3.v_cache.shape)) for _ in range(8)]
+        f = ctypes.c_float
+        fused, separate = [], []
+        pshape = pa.PaPrologueShape(B, Hq, Hkv, D, 128, w3.k_cache.shape[0])
+        for kcx, vcx in pools:
+            fa = (ctypes.byref(shp), qx.data_ptr(), kn.data_ptr(), vn.data_ptr(), wq.data_ptr(),
+                  wk.data_ptr(), posx.data_ptr(), slx.data_ptr(), f(1e-6), f(1e6), f(1.0),
+                  kcx.data_ptr(), vcx.data_ptr(), btx.data_ptr(), ctxx.data_ptr(), f(w3.scale),
+                  ox.data_ptr(), wsx.data_ptr(), wsx.numel(), stream)
+            fused.append(lambda a=fa: pa.lib.pa_decode_step(*a))
+            pa_ = (ctypes.byref(pshape), qx.data_ptr(), kn.data_ptr(), vn.data_ptr(),
+                   wq.data_ptr(), wk.data_ptr(), posx.data_ptr(), slx.data_ptr(), f(1e-6),
+                   f(1e6), f(1.0), qox.data_ptr(), kcx.data_ptr(), vcx.data_ptr(), stream)
+            da = (ctypes.byref(shp), qox.data_ptr(), kcx.data_ptr(), vcx.data_ptr(),
+                  btx.data_ptr(), ctxx.data_ptr(), f(w3.scale), ox.data_ptr(), wsx.data_ptr(),
+                  wsx.numel(), stream)
+            separate.append(lambda a=pa_, b=da: (pa.lib.pa_attention_prologue(*a),
+                                                 pa.lib.pa_decode(*b)))
+        ms_f = timed(torch, fused, 200, 16)
+        ms_s = timed(torch, separate, 200, 16)
+        by = w3.kv_bytes()
+        extra["decode_step_config3"] = {
+            "description": "pa_decode_step (QK-norm, NeoX RoPE and KV write of each sequence's "
+                           "new token fused into decode) at B=16, ctx 4096, 40/8/128",
+            "us_per_call": round(ms_f * 1e3, 2),
+            "separate_prologue_then_decode_us": round(ms_s * 1e3, 2),
+            "kv_bytes_per_call": by,
+            "kv_gbs": round(by / (ms_f * 1e-3) / 1e9, 1),
+        }
+        print(f"[bench] decode step (fused): {ms_f * 1e3:.2f} us/call, prologue + decode "
+              f"{ms_s * 1e3:.2f} us", file=sys.stderr, flush=True)
+        del pools, fused, separate, wsx
+        torch.cuda.empty_cache()
         result["other_workloads"] = extra
 
     if args.calibrate_copy:
