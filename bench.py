@@ -91,12 +91,12 @@ def write_traffic(fetch_dir, write_dir):
     same run (1 GiB read, 1 GiB written), so the result is in true bytes.
     """
     import statistics
-    out = {"kernel": "partition_kernel<128, 5, false>", "workload": "batch 16 x 4096, 40/8 heads, D 128",
+    out = {"kernel": "partition_kernel<128, 5, false, false>", "workload": "batch 16 x 4096, 40/8 heads, D 128",
            "kernel_source_sha256_16": kernel_source_hash()}
     per = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, name)
-        part = [v for k, g, v in rows if "partition_kernel<128, 5, false>" in k]
+        part = [v for k, g, v in rows if "partition_kernel<128, 5, false, false>" in k]
         copy = [v for k, g, v in rows if "copy" in k.lower() and "partition" not in k
                 and "reduce" not in k]
         if not part or not copy:
@@ -265,7 +265,7 @@ def main():
             "kv_bytes_per_call": kv_bytes,
         },
         "roofline": {
-            "kernel": "partition_kernel<128,5,false> (BF16 pools)",
+            "kernel": "partition_kernel<128,5,false,false> (BF16 pools)",
             "bound": "hbm",
             "achieved": round(part_gbs, 1),
             "peak": HBM_PEAK_GBS,
