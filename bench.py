@@ -408,6 +408,21 @@ def main():
                 "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
             }
             print(f"[bench] kv_write T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+            # the same write into FP8-E4M3 pools: 2 BF16 rows read, 2 code rows written
+            kq = torch.empty(512, 128, Hkv, D, dtype=torch.uint8, device=dev)
+            vq = torch.empty_like(kq)
+            qargs = (ctypes.byref(wshape), kn.data_ptr(), vn.data_ptr(), ctypes.c_float(0.0137),
+                     ctypes.c_float(0.0078), slots.data_ptr(), kq.data_ptr(), vq.data_ptr(), stream)
+            ms = timed(torch, [lambda: pa.lib.pa_kv_write_fp8(*qargs)], 200, 10)
+            moved = 2 * T * row_bytes + T * row_bytes
+            extra[f"kv_write_fp8_T{T}"] = {
+                "description": f"FP8-E4M3 paged KV write of {T} tokens, Hkv 8, D 128, random distinct slots",
+                "us_per_call": round(ms * 1e3, 2),
+                "bytes_moved_per_call": moved,
+                "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+            }
+            print(f"[bench] kv_write_fp8 T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+            del kq, vq
         del kc, vc
 
         # multi-query attention (multi-token decode, chunked prefill): cold

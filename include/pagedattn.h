@@ -211,6 +211,24 @@ pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, con
                         const int32_t* slot_mapping, void* k_cache, void* v_cache,
                         void* stream);
 
+/* pa_kv_write into FP8-E4M3 pools (the fp8_e4m3 KV dtype that the orcarouter
+ * page measures decode with; "Qwen 3" TensorSharp docs, section 11: the same
+ * slot addressing). Each BF16 value x of k_new (v_new) is stored as one byte,
+ * the E4M3 ("FN": bias 7, no infinity, 0x7F/0xFF NaN) code of
+ *   y = x / k_scale   (x / v_scale), the quotient an IEEE FP32 division,
+ * saturated to [-448, 448], rounded to the nearest value, ties to the even
+ * code; the sign of y is kept (-0.0 gives 0x80) and NaN gives 0x7F. The code
+ * stands for code * k_scale as pa_decode_fp8 and pa_mq_attention_fp8 read it.
+ *   k_scale,      finite FP32 > 0, else PA_ERR_INVALID_ARGUMENT
+ *   v_scale
+ *   k_codes,      device, uint8 [N, P, Hkv, D], 16-byte aligned; updated in place
+ *   v_codes
+ * Everything else (shapes, slots, alignment, errors) is as for pa_kv_write. */
+pa_status_t pa_kv_write_fp8(const pa_kv_write_shape_t* shape, const void* k_new,
+                            const void* v_new, float k_scale, float v_scale,
+                            const int32_t* slot_mapping, void* k_codes, void* v_codes,
+                            void* stream);
+
 /* ---- multi-query attention (chunked prefill, multi-token decode) ----------
  * Several query tokens per sequence over the same paged cache. The query
  * tokens of all sequences are packed token-major ("Qwen3-14B" pypto-lib page,

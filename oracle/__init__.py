@@ -9,14 +9,17 @@ from .decode import (  # noqa: F401
     attend,
     contiguous_decode_attention,
     decode_fp8_e4m3,
+    encode_fp8_e4m3,
     gather_sequence,
     lse_merge,
     paged_decode_attention,
     paged_decode_attention_fp8,
     paged_kv_write,
+    paged_kv_write_fp8,
     paged_multi_query_attention,
     paged_multi_query_attention_fp8,
     partial_attention,
+    quantize_fp8_e4m3,
 )
 from .prologue import (  # noqa: F401
     attention_prologue,

@@ -77,6 +77,9 @@ __all__ = [
     "lse_merge",
     "paged_kv_write",
     "decode_fp8_e4m3",
+    "encode_fp8_e4m3",
+    "quantize_fp8_e4m3",
+    "paged_kv_write_fp8",
     "paged_decode_attention_fp8",
     "paged_multi_query_attention",
 ]
@@ -295,6 +298,53 @@ def decode_fp8_e4m3(codes) -> np.ndarray:
     val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
     val = s * val
     return np.where((e == 15) & ((b & 7) == 7), np.nan, val)
+
+
+def encode_fp8_e4m3(y) -> np.ndarray:
+    """FP32 values to FP8 E4M3 ("FN") bytes: saturate, round to nearest even.
+
+    The value set is the one ``decode_fp8_e4m3`` defines. |y| is first limited
+    to 448, the largest finite value (the format has no infinity, so overflow
+    saturates); the result is the code of the nearest value, and of the two
+    neighbours of an exact midpoint the one whose code (hence mantissa) is
+    even. The sign bit is y's, so -0.0 gives 0x80. NaN gives 0x7F. Reading: the
+    pages name the dtype but not its rounding; nearest-even with saturation is
+    the plainest one for a cache that must hold every finite input.
+    """
+    y = np.asarray(y, dtype=np.float32).astype(np.float64)       # exact widening
+    pos = decode_fp8_e4m3(np.arange(0x7F))                         # codes 0..0x7E, increasing
+    a = np.minimum(np.abs(y), pos[-1])
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 1, 0x7E)   # first value >= a
+    lo = hi - 1
+    d_lo = a - pos[lo]
+    d_hi = pos[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo) | (np.signbit(y).astype(np.int64) << 7)
+    code = np.where(np.isnan(y), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_fp8_e4m3(x, scale) -> np.ndarray:
+    """Codes of x / scale: x widened to FP32, the quotient taken in FP32
+    (IEEE division, round to nearest even), then ``encode_fp8_e4m3``. The
+    stored code stands for code * scale, as ``paged_decode_attention_fp8``
+    reads it."""
+    x32 = np.asarray(x, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        q = x32 / np.float32(scale)
+    return encode_fp8_e4m3(q)
+
+
+def paged_kv_write_fp8(k_codes, v_codes, k_new, v_new, k_scale, v_scale, slot_mapping):
+    """``paged_kv_write`` into FP8-E4M3 pools: the rows written are
+    ``quantize_fp8_e4m3(k_new, k_scale)`` and ``quantize_fp8_e4m3(v_new,
+    v_scale)``; the same slot rules (negative or past the pool: nothing
+    written). Returns new (k_codes, v_codes) uint8 arrays."""
+    with np.errstate(invalid="ignore"):                 # signalling NaN inputs widen quietly
+        kq = quantize_fp8_e4m3(_as_f64(k_new), k_scale)
+        vq = quantize_fp8_e4m3(_as_f64(v_new), v_scale)
+    return paged_kv_write(np.asarray(k_codes, dtype=np.uint8), np.asarray(v_codes, dtype=np.uint8),
+                          kq, vq, slot_mapping)
 
 
 def paged_decode_attention_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table,

@@ -421,12 +421,17 @@ pa_status_t pa_merge_partials(const pa_shape_t* shape, const int32_t* context_le
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
-pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
-                        const int32_t* slot_mapping, void* k_cache, void* v_cache,
-                        void* stream) {
+namespace {
+
+pa_status_t kv_write_call(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
+                          bool fp8, float k_scale, float v_scale, const int32_t* slot_mapping,
+                          void* k_cache, void* v_cache, void* stream) {
   if (!shape) return PA_ERR_NULL_POINTER;
   if (shape->num_tokens < 0 || shape->num_kv_heads < 1 || shape->head_dim < 1 ||
       shape->page_size < 1 || shape->num_pages < 1)
+    return PA_ERR_INVALID_ARGUMENT;
+  // a scale is a divisor: finite and positive
+  if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.0f && v_scale > 0.0f))
     return PA_ERR_INVALID_ARGUMENT;
   if (shape->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
   if (shape->head_dim % 8 != 0 || shape->head_dim > 1024 || shape->num_kv_heads > 4096)
@@ -450,8 +455,28 @@ pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, con
   a.head_dim = shape->head_dim;
   a.page_size = shape->page_size;
   a.num_pages = shape->num_pages;
+  a.fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.stream = stream;
   return pa::launch_kv_write(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
+                        const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                        void* stream) {
+  return kv_write_call(shape, k_new, v_new, false, 1.0f, 1.0f, slot_mapping, k_cache, v_cache,
+                       stream);
+}
+
+pa_status_t pa_kv_write_fp8(const pa_kv_write_shape_t* shape, const void* k_new,
+                            const void* v_new, float k_scale, float v_scale,
+                            const int32_t* slot_mapping, void* k_codes, void* v_codes,
+                            void* stream) {
+  return kv_write_call(shape, k_new, v_new, true, k_scale, v_scale, slot_mapping, k_codes,
+                       v_codes, stream);
 }
 
 pa_status_t pa_mq_plan(const pa_mq_shape_t* shape, pa_plan_t* plan) {

@@ -8,6 +8,13 @@
 // write is a row copy. Every thread copies one 16-byte chunk of K and the same
 // chunk of V; a negative slot (padding) or a slot past the pool writes nothing.
 // HBM-bound: per token 2 rows read and 2 rows written.
+//
+// FP8 pools (one byte per value, E4M3 "FN" encoding, one FP32 scale per pool):
+// each BF16 value x is stored as the code of x / scale, the quotient taken in
+// FP32 with IEEE division, saturated to +-448 (the format has no infinity),
+// rounded to nearest even by v_cvt_pk_fp8_f32; NaN is stored as 0x7F. The
+// decode and multi-query kernels read code * scale back, so the cache keeps
+// the fp8_e4m3 KV dtype the orcarouter page measures against NVFP4 KV.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,6 +25,7 @@ namespace pa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWriteThreads = 256;
 
@@ -37,6 +45,52 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(
   v_cache[slot * chunks_per_row + c] = vv;
 }
 
+// E4M3 codes of four FP32 values, byte j from y[j]. The explicit clamp makes
+// the conversion's own overflow handling irrelevant; NaN is set after it.
+__device__ __forceinline__ uint32_t e4m3x4(const float* y) {
+  float c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = __builtin_fminf(__builtin_fmaxf(y[j], -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  uint32_t u = (uint32_t)w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (__builtin_isnan(y[j])) u = (u & ~(0xFFu << (8 * j))) | (0x7Fu << (8 * j));
+  return u;
+}
+
+// Eight BF16 values (one 16-byte chunk) divided by `scale` and encoded.
+__device__ __forceinline__ u32x2 quantize8(u32x4 x, float scale) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    y[2 * j] = __uint_as_float(x[j] << 16) / scale;
+    y[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u) / scale;
+  }
+  u32x2 r;
+  r[0] = e4m3x4(y);
+  r[1] = e4m3x4(y + 4);
+  return r;
+}
+
+__global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
+    const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+    const int32_t* __restrict__ slot_mapping, u32x2* __restrict__ k_codes,
+    u32x2* __restrict__ v_codes, long long total_chunks, int chunks_per_row, long long num_slots,
+    float k_scale, float v_scale) {
+  const long long i = (long long)blockIdx.x * kWriteThreads + threadIdx.x;
+  if (i >= total_chunks) return;
+  const long long t = i / chunks_per_row;
+  const int c = (int)(i - t * chunks_per_row);
+  const long long slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding token / outside the pool
+  const u32x4 kv = k_new[i];
+  const u32x4 vv = v_new[i];
+  k_codes[slot * chunks_per_row + c] = quantize8(kv, k_scale);
+  v_codes[slot * chunks_per_row + c] = quantize8(vv, v_scale);
+}
+
 }  // namespace
 
 int launch_kv_write(const KvWriteArgs& a) {
@@ -44,6 +98,15 @@ int launch_kv_write(const KvWriteArgs& a) {
   const long long total = (long long)a.num_tokens * chunks_per_row;
   const long long num_slots = (long long)a.num_pages * a.page_size;
   const unsigned grid = (unsigned)((total + kWriteThreads - 1) / kWriteThreads);
+  if (a.fp8) {
+    void* args[] = {(void*)&a.k_new,   (void*)&a.v_new,   (void*)&a.slot_mapping,
+                    (void*)&a.k_cache, (void*)&a.v_cache, (void*)&total,
+                    (void*)&chunks_per_row, (void*)&num_slots, (void*)&a.k_scale,
+                    (void*)&a.v_scale};
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(&kv_write_fp8_kernel), dim3(grid),
+                                dim3(kWriteThreads), args, 0,
+                                reinterpret_cast<hipStream_t>(a.stream));
+  }
   void* args[] = {(void*)&a.k_new,   (void*)&a.v_new,   (void*)&a.slot_mapping,
                   (void*)&a.k_cache, (void*)&a.v_cache, (void*)&total,
                   (void*)&chunks_per_row, (void*)&num_slots};

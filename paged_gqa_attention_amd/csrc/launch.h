@@ -70,9 +70,11 @@ struct KvWriteArgs {
   const void* k_new;          // bf16 [T, Hkv, D]
   const void* v_new;          // bf16 [T, Hkv, D]
   const int32_t* slot_mapping;// int32 [T]
-  void* k_cache;              // bf16 [N, P, Hkv, D]
-  void* v_cache;              // bf16 [N, P, Hkv, D]
+  void* k_cache;              // bf16 [N, P, Hkv, D], or E4M3 codes when fp8
+  void* v_cache;              // bf16 [N, P, Hkv, D], or E4M3 codes when fp8
   int num_tokens, num_kv_heads, head_dim, page_size, num_pages;
+  bool fp8 = false;           // store codes of x / k_scale, x / v_scale
+  float k_scale = 1.0f, v_scale = 1.0f;
   void* stream;               // hipStream_t
 };
 

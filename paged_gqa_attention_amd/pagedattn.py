@@ -8,7 +8,7 @@ the library is missing, importing the binding raises instead of falling back.
 
 Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_decode_step``, ``pa_plan``,
 ``pa_workspace_size``, ``pa_decode_partials``, ``pa_merge_partials``,
-``pa_kv_write``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_mq_attention_fp8``,
+``pa_kv_write``, ``pa_kv_write_fp8``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_mq_attention_fp8``,
 ``pa_attention_prologue``, ``pa_status_string``, ``pa_abi_version``.
 """
 
@@ -139,6 +139,11 @@ def _load():
     lib.pa_kv_write.argtypes = [
         ctypes.POINTER(PaKvWriteShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.pa_kv_write_fp8.restype = ctypes.c_int
+    lib.pa_kv_write_fp8.argtypes = [
+        ctypes.POINTER(PaKvWriteShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
     lib.pa_mq_plan.restype = ctypes.c_int
     lib.pa_mq_plan.argtypes = [ctypes.POINTER(PaMqShape), ctypes.POINTER(PaPlan)]
@@ -414,19 +419,14 @@ def pa_merge_partials(shape: PaShape, context_lens: torch.Tensor, workspace: tor
     return out
 
 
-def pa_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
-                k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
-    """Write new K/V rows [T, Hkv, D] into the pools at flat slots (in place).
-
-    slot = page * 128 + position; negative slots are padding and write nothing.
-    """
+def _kv_write_checks(k_new, v_new, slot_mapping, k_cache, v_cache, cache_dtype):
     if k_new.dim() != 3 or v_new.shape != k_new.shape or k_cache.dim() != 4 \
             or v_cache.shape != k_cache.shape or k_cache.shape[2:] != k_new.shape[1:]:
         raise ValueError("expected k_new/v_new [T, Hkv, D] and caches [N, P, Hkv, D]")
     if slot_mapping.shape != (k_new.shape[0],):
         raise ValueError("slot_mapping must be [T]")
     for name, t, dt in (("k_new", k_new, torch.bfloat16), ("v_new", v_new, torch.bfloat16),
-                        ("k_cache", k_cache, torch.bfloat16), ("v_cache", v_cache, torch.bfloat16),
+                        ("k_cache", k_cache, cache_dtype), ("v_cache", v_cache, cache_dtype),
                         ("slot_mapping", slot_mapping, torch.int32)):
         if t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
@@ -435,12 +435,34 @@ def pa_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Te
         if t.device != k_new.device or t.device.type != "cuda":
             raise ValueError(f"{name} must be on the GPU of k_new")
     T, Hkv, D = k_new.shape
-    shape = PaKvWriteShape(int(T), int(Hkv), int(D), int(k_cache.shape[1]), int(k_cache.shape[0]))
+    return PaKvWriteShape(int(T), int(Hkv), int(D), int(k_cache.shape[1]), int(k_cache.shape[0]))
+
+
+def pa_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write new K/V rows [T, Hkv, D] into the pools at flat slots (in place).
+
+    slot = page * 128 + position; negative slots are padding and write nothing.
+    """
+    shape = _kv_write_checks(k_new, v_new, slot_mapping, k_cache, v_cache, torch.bfloat16)
     st = _lib.pa_kv_write(ctypes.byref(shape), k_new.data_ptr(), v_new.data_ptr(),
                           slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                           _stream(k_new.device))
     if st != PA_OK:
         raise PagedAttnError(st, "pa_kv_write")
+
+
+def pa_kv_write_fp8(k_new: torch.Tensor, v_new: torch.Tensor, k_scale: float, v_scale: float,
+                    slot_mapping: torch.Tensor, k_codes: torch.Tensor,
+                    v_codes: torch.Tensor) -> None:
+    """Write new BF16 K/V rows [T, Hkv, D] into FP8-E4M3 pools (uint8 codes of
+    x / k_scale and x / v_scale, saturating, nearest-even) at flat slots."""
+    shape = _kv_write_checks(k_new, v_new, slot_mapping, k_codes, v_codes, torch.uint8)
+    st = _lib.pa_kv_write_fp8(ctypes.byref(shape), k_new.data_ptr(), v_new.data_ptr(),
+                              float(k_scale), float(v_scale), slot_mapping.data_ptr(),
+                              k_codes.data_ptr(), v_codes.data_ptr(), _stream(k_new.device))
+    if st != PA_OK:
+        raise PagedAttnError(st, "pa_kv_write_fp8")
 
 
 def mq_shape_of(q, k_cache, block_table, max_query_len: int, split_pages: int = 0) -> PaMqShape:

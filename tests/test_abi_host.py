@@ -5,6 +5,7 @@ call here fails validation on the host before any HIP call.
 """
 
 import ctypes
+import math
 import os
 import re
 
@@ -34,7 +35,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == ["pa_abi_version", "pa_attention_prologue", "pa_decode", "pa_decode_fp8",
-                     "pa_decode_partials", "pa_decode_step", "pa_kv_write", "pa_merge_partials", "pa_mq_attention",
+                     "pa_decode_partials", "pa_decode_step", "pa_kv_write", "pa_kv_write_fp8",
+                     "pa_merge_partials", "pa_mq_attention",
                      "pa_mq_attention_fp8", "pa_mq_plan", "pa_plan", "pa_status_string",
                      "pa_workspace_size"]
 
@@ -222,6 +224,34 @@ def test_kv_write_rejects_bad_arguments():
         a[i] = bad
         assert call(good(), *a) == pa.PA_ERR_INVALID_ARGUMENT, i
     assert call(pa.PaKvWriteShape(0, 8, 128, 128, 64), None, None, None, None, None, None) == pa.PA_OK
+
+
+@fake_pointers
+def test_kv_write_fp8_rejects_bad_arguments():
+    d = 1 << 20
+    def call(shape, ks, vs, *ptrs):
+        k_new, v_new, slots, kc, vc, stream = ptrs
+        return pa.lib.pa_kv_write_fp8(ctypes.byref(shape) if shape is not None else None, k_new,
+                                      v_new, ks, vs, slots, kc, vc, stream)
+    ok = [d, d, d, d, d, None]
+    good = lambda: pa.PaKvWriteShape(16, 8, 128, 128, 64)
+    assert call(None, 1.0, 1.0, *ok) == pa.PA_ERR_NULL_POINTER
+    for ks, vs in ((0.0, 1.0), (1.0, -0.5), (math.inf, 1.0), (1.0, math.nan), (-0.0, 1.0)):
+        assert call(good(), ks, vs, *ok) == pa.PA_ERR_INVALID_ARGUMENT, (ks, vs)
+    for field, value, code in (("num_tokens", -1, 2), ("page_size", 64, 3), ("head_dim", 12, 3)):
+        s = good()
+        setattr(s, field, value)
+        assert call(s, 1.0, 1.0, *ok) == code, field
+    for i in range(5):
+        a = list(ok)
+        a[i] = None
+        assert call(good(), 1.0, 1.0, *a) == pa.PA_ERR_NULL_POINTER, i
+    for i, bad in ((0, d + 8), (1, d + 2), (2, d + 2), (3, d + 8), (4, d + 4)):
+        a = list(ok)
+        a[i] = bad
+        assert call(good(), 1.0, 1.0, *a) == pa.PA_ERR_INVALID_ARGUMENT, i
+    assert call(pa.PaKvWriteShape(0, 8, 128, 128, 64), 0.5, 2.0, None, None, None, None, None,
+                None) == pa.PA_OK
 
 
 # ---- multi-query entry points ------------------------------------------------
