@@ -166,22 +166,6 @@ __device__ __forceinline__ f32x4 merge_result(const MergeState& st, int nv) {
   return res;
 }
 
-template <int D, int C = kMergeChunk>
-__device__ __forceinline__ f32x4 merge_row(const float* __restrict__ ws_acc,
-                                           const float* __restrict__ ws_ml, size_t row,
-                                           int num_splits, int nv, int d4) {
-  const float* ml = ws_ml + row * num_splits * 2;
-  const float* acc = ws_acc + row * num_splits * D + d4;
-  MergeState st;
-  for (int s0 = 0; s0 < nv; s0 += C) {
-    float2 mlv[C];
-    f32x4 av[C];
-    merge_load<D, C>(ml, acc, s0, nv - s0, mlv, av);
-    merge_fold<C>(st, mlv, av, nv - s0);
-  }
-  return merge_result(st, nv);
-}
-
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 v) {
   uint2 packed;
   packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);

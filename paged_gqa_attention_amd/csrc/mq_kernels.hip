@@ -846,31 +846,66 @@ __global__ __launch_bounds__(kM32Threads) void mq32_kernel(
 }
 
 // Merge of the splits of every (query token, query head) row: one thread per 4
-// dims. The row's sequence is found by binary search in query_start.
+// dims, kMqReduceThreads / (D / 4) rows per workgroup. The first partials of
+// the row load before its sequence is known (they depend only on the row);
+// for up to kMqReduceScan sequences, query_start loads in the same round trip
+// and the sequence is counted with ballots, else it is found by binary search.
+constexpr int kMqReduceThreads = 128;
+constexpr int kMqReduceScan = 256;
+
 template <int D>
-__global__ __launch_bounds__(256) void mq_reduce_kernel(
+__global__ __launch_bounds__(kMqReduceThreads) void mq_reduce_kernel(
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
     uint16_t* __restrict__ out, int batch, int num_tokens, int num_q_heads, int max_query_len,
     int num_splits, int split_tokens, int max_ctx) {
   constexpr int TPR = D / 4;
-  constexpr int RPW = 256 / TPR;
+  constexpr int RPW = kMqReduceThreads / TPR;
+  constexpr int C = kMergeChunk;
+  static_assert(64 % TPR == 0 && 64 / TPR <= 2, "a wave holds one or two rows");
+  const int rows = num_tokens * num_q_heads;
+  const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * RPW + (int)threadIdx.x / TPR;
-  if (row >= num_tokens * num_q_heads) return;
   const int d4 = ((int)threadIdx.x % TPR) * 4;
-  const int t = row / num_q_heads;
-  // last b with query_start[b] <= t
-  int lo = 0, hi = batch;  // answer in [0, batch)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (query_start[mid] <= t) lo = mid;
-    else hi = mid;
+  const int t = min(row, rows - 1) / num_q_heads;
+  const float* ml = ws_ml + (size_t)row * num_splits * 2;
+  const float* acc = ws_acc + (size_t)row * num_splits * D + d4;
+  float2 mlv[C];
+  f32x4 av[C];
+  if (row < rows) merge_load<D, C>(ml, acc, 0, num_splits, mlv, av);
+  // sequence of token t: the last b in [0, batch) with query_start[b] <= t
+  int lo = 0;
+  if (batch <= kMqReduceScan) {
+    int qv[kMqReduceScan / 64];
+#pragma unroll
+    for (int c = 0; c < kMqReduceScan / 64; ++c) {
+      const int e = 64 * c + lane;
+      qv[c] = (e >= 1 && e < batch) ? query_start[e] : INT32_MAX;  // b = 0 always counts
+    }
+    // the wave's rows belong to at most two tokens: its first and last lane's
+    const int t0 = __builtin_amdgcn_readfirstlane(t);
+    const int t1 = __builtin_amdgcn_readlane(t, 63);
+    int n0 = 0, n1 = 0;
+#pragma unroll
+    for (int c = 0; c < kMqReduceScan / 64; ++c) {
+      n0 += __popcll(__ballot(qv[c] <= t0));
+      n1 += __popcll(__ballot(qv[c] <= t1));
+    }
+    lo = t == t0 ? n0 : n1;
+  } else {
+    int hi = batch;  // answer in [0, batch)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (query_start[mid] <= t) lo = mid;
+      else hi = mid;
+    }
   }
+  if (row >= rows) return;
   const int qs0 = query_start[lo];
   const int lqn = query_start[lo + 1] - qs0;
+  const int ctx = context_lens[lo];
   if (qs0 < 0 || lqn <= 0 || lqn > max_query_len || qs0 > num_tokens - lqn) return;
   if (t < qs0 || t >= qs0 + lqn) return;  // not covered by a sequence
-  const int ctx = context_lens[lo];
   f32x4 res;
   if (ctx < 0 || ctx > max_ctx) {
     const float nan = __builtin_nanf("");
@@ -879,7 +914,13 @@ __global__ __launch_bounds__(256) void mq_reduce_kernel(
     const int n_row = ctx - lqn + (t - qs0) + 1;
     int nv = n_row <= 0 ? 0 : (n_row + split_tokens - 1) / split_tokens;
     nv = nv > num_splits ? num_splits : nv;
-    res = merge_row<D>(ws_acc, ws_ml, (size_t)row, num_splits, nv, d4);
+    MergeState st;
+    merge_fold<C>(st, mlv, av, nv);
+    for (int s0 = C; s0 < nv; s0 += C) {
+      merge_load<D, C>(ml, acc, s0, nv - s0, mlv, av);
+      merge_fold<C>(st, mlv, av, nv - s0);
+    }
+    res = merge_result(st, nv);
   }
   store_bf16x4(out + (size_t)row * D + d4, res);
 }
@@ -938,13 +979,14 @@ int launch_mq_reduce_d(const MqLaunchArgs& a) {
   const int rows = a.num_tokens * a.num_q_heads;
   const int split_tokens = a.split_pages * kMqPage;
   const int max_ctx = a.max_pages * kMqPage;
-  constexpr int RPW = 256 / (D / 4);
+  constexpr int RPW = kMqReduceThreads / (D / 4);
   void* args[] = {(void*)&a.ws_acc,        (void*)&a.ws_ml,       (void*)&a.context_lens,
                   (void*)&a.query_start,   (void*)&a.out,         (void*)&a.batch,
                   (void*)&a.num_tokens,    (void*)&a.num_q_heads, (void*)&a.max_query_len,
                   (void*)&a.num_splits,    (void*)&split_tokens,  (void*)&max_ctx};
   return (int)hipLaunchKernel(reinterpret_cast<const void*>(&mq_reduce_kernel<D>),
-                              dim3((rows + RPW - 1) / RPW), dim3(256), args, 0, stream);
+                              dim3((rows + RPW - 1) / RPW), dim3(kMqReduceThreads), args, 0,
+                              stream);
 }
 
 }  // namespace

@@ -211,6 +211,20 @@ def test_longest_first_dispatch_ragged(B):
     assert_parity(run_mq(w), ref, f"mq ordered B={B}")
 
 
+@pytest.mark.parametrize("B,sp", [(63, 1), (64, 1), (200, 1), (257, 1), (300, 2)])
+def test_merge_finds_the_sequence_of_every_row(B, sp):
+    # the merge kernel locates each row's sequence by counting query_start
+    # entries (up to 256 sequences, several 64-entry rounds) or by binary
+    # search (more); empty chunks and one-token chunks mixed in
+    rng = np.random.default_rng(B + 7)
+    lq = [int(rng.integers(0, 4)) for _ in range(B)]
+    lq[0], lq[-1] = max(lq[0], 1), max(lq[-1], 2)
+    ctx = [int(rng.integers(max(q, 1), 380)) for q in lq]
+    announce(f"mq merge row search B={B} sp{sp}")
+    w = workloads.build_mq(lq, ctx, 16, 2, 128, seed=400 + B, max_pages=3, pool="packed")
+    assert_parity(run_mq(w, split_pages=sp), oracle_mq(w), f"mq merge search B={B}")
+
+
 def test_shared_prefix_pages():
     # two sequences share their first pages (a common prefix), then diverge
     announce("mq shared prefix")
