@@ -153,6 +153,16 @@ def timed(torch, fns, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def timed_pair(torch, fns_a, fns_b, steps=200, warmup=32):
+    """Average ms per call of two alternatives, each timed twice in the order
+    a, b, a, b (clock and cache warm-up then affect both alike)."""
+    a1 = timed(torch, fns_a, steps, warmup)
+    b1 = timed(torch, fns_b, steps, warmup)
+    a2 = timed(torch, fns_a, steps, warmup)
+    b2 = timed(torch, fns_b, steps, warmup)
+    return (a1 + a2) / 2, (b1 + b2) / 2
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -531,8 +541,7 @@ def main():
                   wsx.numel(), stream)
             separate.append(lambda a=pa_, b=da: (pa.lib.pa_attention_prologue(*a),
                                                  pa.lib.pa_decode(*b)))
-        ms_f = timed(torch, fused, 200, 16)
-        ms_s = timed(torch, separate, 200, 16)
+        ms_f, ms_s = timed_pair(torch, fused, separate)
         by = w3.kv_bytes()
         extra["decode_step_config3"] = {
             "description": "pa_decode_step (QK-norm, NeoX RoPE and KV write of each sequence's "
@@ -544,7 +553,43 @@ def main():
         }
         print(f"[bench] decode step (fused): {ms_f * 1e3:.2f} us/call, prologue + decode "
               f"{ms_s * 1e3:.2f} us", file=sys.stderr, flush=True)
-        del pools, fused, separate, wsx
+        del pools, fused, separate
+
+        # the same step over FP8-E4M3 pools (pa_decode_step_fp8 against
+        # pa_attention_prologue_fp8 followed by pa_decode_fp8)
+        ks8, vs8 = 0.0125, 0.0125
+        pools8 = [tuple(torch.randint(0, 256, w3.k_cache.shape, device=dev, generator=gen,
+                                      dtype=torch.uint8) & 0x77 for _ in range(2))
+                  for _ in range(8)]          # & 0x77: finite codes only
+        fused, separate = [], []
+        for kcx, vcx in pools8:
+            fa = (ctypes.byref(shp), qx.data_ptr(), kn.data_ptr(), vn.data_ptr(), wq.data_ptr(),
+                  wk.data_ptr(), posx.data_ptr(), slx.data_ptr(), f(1e-6), f(1e6), f(1.0),
+                  f(ks8), f(vs8), kcx.data_ptr(), vcx.data_ptr(), btx.data_ptr(),
+                  ctxx.data_ptr(), f(w3.scale), ox.data_ptr(), wsx.data_ptr(), wsx.numel(),
+                  stream)
+            fused.append(lambda a=fa: pa.lib.pa_decode_step_fp8(*a))
+            pa_ = (ctypes.byref(pshape), qx.data_ptr(), kn.data_ptr(), vn.data_ptr(),
+                   wq.data_ptr(), wk.data_ptr(), posx.data_ptr(), slx.data_ptr(), f(1e-6),
+                   f(1e6), f(1.0), f(ks8), f(vs8), qox.data_ptr(), kcx.data_ptr(),
+                   vcx.data_ptr(), stream)
+            da = (ctypes.byref(shp), qox.data_ptr(), kcx.data_ptr(), vcx.data_ptr(), f(ks8),
+                  f(vs8), btx.data_ptr(), ctxx.data_ptr(), f(w3.scale), ox.data_ptr(),
+                  wsx.data_ptr(), wsx.numel(), stream)
+            separate.append(lambda a=pa_, b=da: (pa.lib.pa_attention_prologue_fp8(*a),
+                                                 pa.lib.pa_decode_fp8(*b)))
+        ms_f, ms_s = timed_pair(torch, fused, separate)
+        extra["decode_step_fp8_config3"] = {
+            "description": "pa_decode_step_fp8 (the fused step over FP8-E4M3 pools, per-tensor "
+                           "scales) at B=16, ctx 4096, 40/8/128",
+            "us_per_call": round(ms_f * 1e3, 2),
+            "separate_prologue_then_decode_us": round(ms_s * 1e3, 2),
+            "kv_bytes_per_call": by // 2,
+            "kv_gbs": round(by / 2 / (ms_f * 1e-3) / 1e9, 1),
+        }
+        print(f"[bench] decode step fp8 (fused): {ms_f * 1e3:.2f} us/call, prologue + decode "
+              f"{ms_s * 1e3:.2f} us", file=sys.stderr, flush=True)
+        del pools8, fused, separate, wsx
         torch.cuda.empty_cache()
         result["other_workloads"] = extra
 

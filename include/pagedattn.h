@@ -342,6 +342,23 @@ pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* 
                                   float rope_scale, void* q_out, void* k_cache, void* v_cache,
                                   void* stream);
 
+/* pa_attention_prologue writing FP8-E4M3 pools (the fp8_e4m3 KV dtype of the
+ * orcarouter page). q_out is as above. K is first computed and rounded to
+ * BF16 exactly as above; that BF16 row and v are then stored as
+ * pa_kv_write_fp8 stores them: the code of x / k_scale (x / v_scale), an IEEE
+ * FP32 quotient, saturated to +-448, nearest even, NaN -> 0x7F. The result
+ * equals pa_attention_prologue followed by pa_kv_write_fp8 of its K row and v.
+ *   k_scale, v_scale   finite FP32 > 0, else PA_ERR_INVALID_ARGUMENT
+ *   k_codes, v_codes   device, uint8 [N, P, Hkv, D], 16-byte aligned, updated
+ *                      in place
+ * Everything else as for pa_attention_prologue. */
+pa_status_t pa_attention_prologue_fp8(const pa_prologue_shape_t* shape, const void* q,
+                                      const void* k, const void* v, const void* q_norm_weight,
+                                      const void* k_norm_weight, const int32_t* positions,
+                                      const int32_t* slot_mapping, float eps, float rope_base,
+                                      float rope_scale, float k_scale, float v_scale,
+                                      void* q_out, void* k_codes, void* v_codes, void* stream);
+
 /* A whole decode step's attention in one call: the prologue above for each
  * sequence's new token, fused into pa_decode's first kernel, as the
  * "Qwen3-14B" decode_fwd section runs it (the attention kernel's phase 0).
@@ -367,6 +384,24 @@ pa_status_t pa_decode_step(const pa_shape_t* shape, const void* q, const void* k
                            float rope_scale, void* k_cache, void* v_cache,
                            const int32_t* block_table, const int32_t* context_lens, float scale,
                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_decode_step over FP8-E4M3 pools: the new token's K (after norm and RoPE,
+ * rounded to BF16) and V are stored at its slot as pa_attention_prologue_fp8
+ * stores them, and attention reads the pools as pa_decode_fp8 does (code *
+ * k_scale, code * v_scale), the new token included: its K and V enter as the
+ * values of the codes written. Equals pa_attention_prologue_fp8 followed by
+ * pa_decode_fp8 up to FP32 rounding, in one launch plus the merge.
+ *   k_scale, v_scale   finite FP32 > 0, else PA_ERR_INVALID_ARGUMENT
+ *   k_codes, v_codes   device, uint8 [N, P, Hkv, D], 16-byte aligned
+ * Everything else as for pa_decode_step. */
+pa_status_t pa_decode_step_fp8(const pa_shape_t* shape, const void* q, const void* k_new,
+                               const void* v_new, const void* q_norm_weight,
+                               const void* k_norm_weight, const int32_t* positions,
+                               const int32_t* slot_mapping, float eps, float rope_base,
+                               float rope_scale, float k_scale, float v_scale, void* k_codes,
+                               void* v_codes, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,9 @@ from .decode import (  # noqa: F401
 )
 from .prologue import (  # noqa: F401
     attention_prologue,
+    attention_prologue_fp8,
     rms_norm_heads,
     rope_angles,
     rope_neox,
+    round_bf16,
 )

@@ -44,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .decode import paged_kv_write
+from .decode import paged_kv_write, paged_kv_write_fp8
 
 __all__ = ["rms_norm_heads", "rope_neox", "rope_angles", "attention_prologue"]
 
@@ -96,4 +96,29 @@ def attention_prologue(q, k, v, q_norm_w, k_norm_w, positions, slot_mapping, eps
     q_out = rope_neox(rms_norm_heads(q, q_norm_w, eps), positions, rope_base, rope_scale)
     k_rot = rope_neox(rms_norm_heads(k, k_norm_w, eps), positions, rope_base, rope_scale)
     kc, vc = paged_kv_write(_f64(k_cache), _f64(v_cache), k_rot, _f64(v), slot_mapping)
+    return q_out, kc, vc
+
+
+def round_bf16(x) -> np.ndarray:
+    """FP64 values rounded once to the nearest BF16 value (8 significant bits;
+    ties to even; spacing 2^-133 below 2^-126), returned as FP64."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                      # |x| = m * 2^e with 0.5 <= m < 1
+    step = np.maximum(e - 8, -133)          # exponent of the BF16 spacing at x
+    return np.ldexp(np.rint(np.ldexp(x, -step)), step)
+
+
+def attention_prologue_fp8(q, k, v, q_norm_w, k_norm_w, positions, slot_mapping, eps,
+                           rope_base, rope_scale, k_scale, v_scale, k_codes, v_codes):
+    """The prologue writing FP8-E4M3 pools: the K rows of ``attention_prologue``
+    rounded to BF16 (the row the BF16 pools would hold), then stored as
+    ``paged_kv_write_fp8`` stores a BF16 row (codes of x / k_scale); V as
+    given, codes of v / v_scale. Reading: the pages name the fp8_e4m3 cache
+    but not where the rounding happens; quantising the BF16 row makes the FP8
+    prologue the BF16 prologue followed by the FP8 write. Returns (q_out FP64,
+    k_codes, v_codes) with the codes as new uint8 arrays."""
+    q_out = rope_neox(rms_norm_heads(q, q_norm_w, eps), positions, rope_base, rope_scale)
+    k_rot = round_bf16(rope_neox(rms_norm_heads(k, k_norm_w, eps), positions, rope_base,
+                                  rope_scale))
+    kc, vc = paged_kv_write_fp8(k_codes, v_codes, k_rot, _f64(v), k_scale, v_scale, slot_mapping)
     return q_out, kc, vc

@@ -334,13 +334,18 @@ pa_status_t pa_decode(const pa_shape_t* shape, const void* q, const void* k_cach
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
-pa_status_t pa_decode_step(const pa_shape_t* shape, const void* q, const void* k_new,
-                           const void* v_new, const void* q_norm_weight,
-                           const void* k_norm_weight, const int32_t* positions,
-                           const int32_t* slot_mapping, float eps, float rope_base,
-                           float rope_scale, void* k_cache, void* v_cache,
-                           const int32_t* block_table, const int32_t* context_lens, float scale,
-                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t decode_step_call(const pa_shape_t* shape, const void* q, const void* k_new,
+                             const void* v_new, const void* q_norm_weight,
+                             const void* k_norm_weight, const int32_t* positions,
+                             const int32_t* slot_mapping, float eps, float rope_base,
+                             float rope_scale, bool fp8, float k_scale, float v_scale,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             const int32_t* context_lens, float scale, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   pa_status_t st = check_shape(shape);
   if (st != PA_OK) return st;
   if (shape->batch == 0) return PA_OK;
@@ -352,26 +357,67 @@ pa_status_t pa_decode_step(const pa_shape_t* shape, const void* q, const void* k
   if (!isfinite(eps) || eps < 0.f || !isfinite(rope_base) || rope_base <= 0.f ||
       !isfinite(rope_scale) || rope_scale <= 0.f)
     return PA_ERR_INVALID_ARGUMENT;
+  // FP8: the scales divide the new rows before encoding and multiply the codes
+  if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.0f && v_scale > 0.0f))
+    return PA_ERR_INVALID_ARGUMENT;
   pa::LaunchArgs a;
   st = prepare(shape, q, k_cache, v_cache, block_table, context_lens, scale, out, workspace,
                workspace_bytes, stream, true, true, &a);
   if (st != PA_OK) return st;
   const double d = shape->head_dim;
   a.decode_step = true;
+  if (fp8) {
+    a.kv_fp8 = true;
+    a.score_scale = scale * k_scale * 1.4426950408889634f;
+    a.v_scale = v_scale;
+  }
   a.step.k_new = static_cast<const uint16_t*>(k_new);
   a.step.v_new = static_cast<const uint16_t*>(v_new);
   a.step.q_norm_w = static_cast<const uint16_t*>(q_norm_weight);
   a.step.k_norm_w = static_cast<const uint16_t*>(k_norm_weight);
   a.step.positions = positions;
   a.step.slot_mapping = slot_mapping;
-  a.step.k_pool = static_cast<uint16_t*>(k_cache);
-  a.step.v_pool = static_cast<uint16_t*>(v_cache);
+  a.step.k_pool = k_cache;
+  a.step.v_pool = v_cache;
   a.step.num_slots = (long long)shape->num_pages * shape->page_size;
+  a.step.k_scale = fp8 ? k_scale : 1.0f;
+  a.step.v_scale = fp8 ? v_scale : 1.0f;
   a.step.eps = eps;
   a.step.inv_scale = 1.0 / (double)rope_scale;
   a.step.log2r = -2.0 * log2((double)rope_base) / d;
   if (pa::launch_partition(a) != 0) return PA_ERR_LAUNCH;
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_step(const pa_shape_t* shape, const void* q, const void* k_new,
+                           const void* v_new, const void* q_norm_weight,
+                           const void* k_norm_weight, const int32_t* positions,
+                           const int32_t* slot_mapping, float eps, float rope_base,
+                           float rope_scale, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens, float scale,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_step_call(shape, q, k_new, v_new, q_norm_weight, k_norm_weight, positions,
+                          slot_mapping, eps, rope_base, rope_scale, false, 1.0f, 1.0f, k_cache,
+                          v_cache, block_table, context_lens, scale, out, workspace,
+                          workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_step_fp8(const pa_shape_t* shape, const void* q, const void* k_new,
+                               const void* v_new, const void* q_norm_weight,
+                               const void* k_norm_weight, const int32_t* positions,
+                               const int32_t* slot_mapping, float eps, float rope_base,
+                               float rope_scale, float k_scale, float v_scale, void* k_codes,
+                               void* v_codes, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_step_call(shape, q, k_new, v_new, q_norm_weight, k_norm_weight, positions,
+                          slot_mapping, eps, rope_base, rope_scale, true, k_scale, v_scale,
+                          k_codes, v_codes, block_table, context_lens, scale, out, workspace,
+                          workspace_bytes, stream);
 }
 
 pa_status_t pa_decode_fp8(const pa_shape_t* shape, const void* q, const void* k_cache,
@@ -421,6 +467,8 @@ pa_status_t pa_merge_partials(const pa_shape_t* shape, const int32_t* context_le
   return pa::launch_reduce(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
 namespace {
 
 pa_status_t kv_write_call(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
@@ -463,6 +511,8 @@ pa_status_t kv_write_call(const pa_kv_write_shape_t* shape, const void* k_new, c
 }
 
 }  // namespace
+
+extern "C" {
 
 pa_status_t pa_kv_write(const pa_kv_write_shape_t* shape, const void* k_new, const void* v_new,
                         const int32_t* slot_mapping, void* k_cache, void* v_cache,
@@ -508,12 +558,16 @@ pa_status_t pa_mq_attention_fp8(const pa_mq_shape_t* shape, const void* q, const
                  query_start, scale, out, workspace, workspace_bytes, stream);
 }
 
-pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* q, const void* k,
-                                  const void* v, const void* q_norm_weight,
-                                  const void* k_norm_weight, const int32_t* positions,
-                                  const int32_t* slot_mapping, float eps, float rope_base,
-                                  float rope_scale, void* q_out, void* k_cache, void* v_cache,
-                                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status_t prologue_call(const pa_prologue_shape_t* shape, const void* q, const void* k,
+                          const void* v, const void* q_norm_weight, const void* k_norm_weight,
+                          const int32_t* positions, const int32_t* slot_mapping, float eps,
+                          float rope_base, float rope_scale, bool fp8, float k_scale,
+                          float v_scale, void* q_out, void* k_cache, void* v_cache,
+                          void* stream) {
   if (!shape) return PA_ERR_NULL_POINTER;
   if (shape->num_tokens < 0 || shape->num_q_heads < 1 || shape->num_kv_heads < 1 ||
       shape->head_dim < 1 || shape->page_size < 1 || shape->num_pages < 1)
@@ -525,6 +579,8 @@ pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* 
   if (shape->num_q_heads + 2 * shape->num_kv_heads > 1 << 16) return PA_ERR_UNSUPPORTED;
   if (!(eps >= 0.0f) || !isfinite(eps) || !(rope_base > 0.0f) || !isfinite(rope_base) ||
       !(rope_scale > 0.0f) || !isfinite(rope_scale))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.0f && v_scale > 0.0f))
     return PA_ERR_INVALID_ARGUMENT;
   if (shape->num_tokens == 0) return PA_OK;
   if (!q || !k || !v || !q_norm_weight || !k_norm_weight || !positions || !slot_mapping ||
@@ -543,8 +599,8 @@ pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* 
   a.positions = positions;
   a.slot_mapping = slot_mapping;
   a.q_out = static_cast<uint16_t*>(q_out);
-  a.k_cache = static_cast<uint16_t*>(k_cache);
-  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.num_tokens = shape->num_tokens;
   a.num_q_heads = shape->num_q_heads;
   a.num_kv_heads = shape->num_kv_heads;
@@ -554,8 +610,37 @@ pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* 
   a.eps = eps;
   a.rope_base = rope_base;
   a.rope_scale = rope_scale;
+  a.fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.stream = stream;
   return pa::launch_prologue(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_attention_prologue(const pa_prologue_shape_t* shape, const void* q, const void* k,
+                                  const void* v, const void* q_norm_weight,
+                                  const void* k_norm_weight, const int32_t* positions,
+                                  const int32_t* slot_mapping, float eps, float rope_base,
+                                  float rope_scale, void* q_out, void* k_cache, void* v_cache,
+                                  void* stream) {
+  return prologue_call(shape, q, k, v, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                       eps, rope_base, rope_scale, false, 1.0f, 1.0f, q_out, k_cache, v_cache,
+                       stream);
+}
+
+pa_status_t pa_attention_prologue_fp8(const pa_prologue_shape_t* shape, const void* q,
+                                      const void* k, const void* v, const void* q_norm_weight,
+                                      const void* k_norm_weight, const int32_t* positions,
+                                      const int32_t* slot_mapping, float eps, float rope_base,
+                                      float rope_scale, float k_scale, float v_scale,
+                                      void* q_out, void* k_codes, void* v_codes, void* stream) {
+  return prologue_call(shape, q, k, v, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                       eps, rope_base, rope_scale, true, k_scale, v_scale, q_out, k_codes,
+                       v_codes, stream);
 }
 
 }  // extern "C"

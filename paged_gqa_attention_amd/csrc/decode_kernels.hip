@@ -112,9 +112,36 @@ struct Rope {
     }
   }
 
-  // w points at the weights of the lane's dims 8*lq (BF16 [D], 16-byte aligned)
-  __device__ __forceinline__ void norm_rotate(u32x4 (&x)[KK], const uint16_t* w, float eps,
-                                              int lq) const {
+  // First of the 8 dims that lane group lq holds at k-step m of the score
+  // MFMA's operand: BF16 pools 32m + 8lq; FP8 pools 64(m/2) + 16lq + 8(m%2).
+  template <bool kFp8Layout>
+  static __device__ __forceinline__ int dim0(int m, int lq) {
+    return kFp8Layout ? 64 * (m / 2) + 16 * lq + 8 * (m % 2) : 32 * m + 8 * lq;
+  }
+
+  // The norm weights of the lane's dims, loaded ahead of their use (the
+  // loads then overlap the kernel's first memory round trip)
+  struct Weights {
+    u32x4 lo[KH];  // dims dim0(m, lq) .. +7
+    u32x4 hi[KH];  // the same dims + D/2
+  };
+  template <bool kFp8Layout>
+  static __device__ __forceinline__ Weights load_weights(const uint16_t* w, int lq) {
+    Weights r;
+#pragma unroll
+    for (int m = 0; m < KH; ++m) {
+      r.lo[m] = load16(w + dim0<kFp8Layout>(m, lq));
+      r.hi[m] = load16(w + dim0<kFp8Layout>(m, lq) + D / 2);
+    }
+    return r;
+  }
+
+  // x holds the lane's dims dim0(m, lq) .. +7 for m < KK (D/2 apart for m and
+  // m + KH in both layouts). The weights of those dims come from wt when the
+  // caller loaded them ahead (kPreloaded), else from w (BF16 [D]) here.
+  template <bool kFp8Layout, bool kPreloaded>
+  __device__ __forceinline__ void norm_rotate(u32x4 (&x)[KK], const Weights& wt,
+                                              const uint16_t* w, float eps, int lq) const {
     float ss = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -130,17 +157,18 @@ struct Rope {
     const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
 #pragma unroll
     for (int m = 0; m < KH; ++m) {
-      const u32x4 wl = load16(w + 32 * m);
-      const u32x4 wh = load16(w + 32 * (m + KH));
+      const int d = dim0<kFp8Layout>(m, lq);
+      const u32x4 wl = kPreloaded ? wt.lo[m] : load16(w + d);
+      const u32x4 wh = kPreloaded ? wt.hi[m] : load16(w + d + D / 2);
       u32x4 lo_out, hi_out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float o[2][2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          // the lane's dim pair (32m + 8lq + 2i + e, + D/2): angle index = the
-          // first dim, held by lane 32*(m%2) + 8lq + 2i + e (times 64 m/2)
-          const int src = 32 * (m % 2) + 8 * lq + 2 * i + e;
+          // the lane's dim pair (d + 2i + e, + D/2): angle index = the first
+          // dim, held by lane (d + 2i + e) % 64 in its angle m / 2
+          const int src = (d % 64) + 2 * i + e;
           const float cs = __shfl(c_own[m / 2], src);
           const float sn = __shfl(s_own[m / 2], src);
           const float xl = e ? bf16_hi(x[m][i]) : bf16_lo(x[m][i]);
@@ -162,11 +190,13 @@ struct Rope {
 // kFp8: the K/V pools hold FP8 E4M3 codes (one byte per value) with
 // per-tensor scales; k_scale is folded into score_scale on the host and
 // v_scale multiplies the split's output sums. Otherwise they hold BF16.
-// kStep (BF16 pools): the attention prologue of a decode step runs here too.
-// q arrives before RMSNorm and RoPE; every wave normalises and rotates its
-// G query heads itself, and the wave whose split holds the new token (token
-// ctx - 1) normalises and rotates the new K row, writes K and V to the pools
-// at the token's slot, and uses both from registers in its own tiles.
+// kStep: the attention prologue of a decode step runs here too. q arrives
+// before RMSNorm and RoPE; every wave normalises and rotates its G query heads
+// itself, and the wave whose split holds the new token (token ctx - 1)
+// normalises and rotates the new K row, writes K and V to the pools at the
+// token's slot, and uses both from registers in its own tiles. Over FP8 pools
+// the written rows are the codes pa_kv_write_fp8 would store for the BF16
+// rows (K after norm and RoPE), and the registers hold exactly those codes.
 template <int D, int G, bool kFp8, bool kStep>
 __global__ __launch_bounds__(kThreads) void partition_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -176,7 +206,6 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     int num_pages, int split_tokens, int num_splits, float score_scale, float v_scale,
     DecodeStepArgs step) {
   static_assert(D == 128 || D == 256, "head_dim");
-  static_assert(!(kStep && kFp8), "the fused prologue writes BF16 pools");
   static_assert(G >= 1 && G <= 16, "gqa ratio");
   constexpr int ESZ = kFp8 ? 1 : 2;       // bytes per cached K/V value
   constexpr int GP = HeadPad<G>::value;   // LDS row stride (floats)
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     const uint16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)h * G + lr) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = kFp8 ? 64 * (kk >> 1) + 16 * lq + 8 * (kk & 1) : 32 * kk + 8 * lq;
+      const int d0 = Rope<D>::template dim0<kFp8>(kk, lq);
       qa[kk] = (lr < G) ? load16(qrow + d0) : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -261,16 +290,34 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // tnew: the new token's index in this split, or -1 if another split has it.
   // Its K row, V chunk and slot load here; the norm and rotation run once the
   // first K tile's loads are out (the pipeline's ready hook below).
+  // one lane's P.V chunk: 8 values of a token row (16 B of BF16, 8 B of FP8)
+  using VChunk = typename std::conditional<kFp8, u32x2, u32x4>::type;
   int tnew = -1;
-  u32x4 knew[KK];  // new K row in the score MFMA's operand layout (rotated)
+  // q and k norm weights of the lane's dims: loaded with the first loads at
+  // D=128; at D=256 (twice the registers) only when the prologue runs
+  typename Rope<D>::Weights wq_n, wk_n;
+  constexpr bool kEarlyWeights = D == 128;
+  u32x4 knew[KK];  // new K row as score MFMA operand (rotated; FP8: the codes' values)
   VChunk4 vnew;    // this lane's 16 bytes of the new V row (dims 8*(lane % (D/8)))
+  VChunk vsub;     // the same dims as the pool holds them (FP8: codes)
   long long slot = -1;
+  // At D=128 and G <= 8 the new rows go to the pool after the wave's last
+  // load: stores to a line the wave still reads (the new token's tile) slowed
+  // its loads. Otherwise (the registers held to the end would spill) they are
+  // written at once.
+  constexpr bool kDeferWrite = D == 128 && G <= 8;
+  constexpr int CW = 2 * KK;  // FP8: code words of the new K row per MFMA lane group
+  uint32_t kcodes[CW];        // FP8: those code words (dims 64m + 16lq + 4w: word 4m + w)
+  bool pool_write = false;
   if constexpr (kStep) {
+    if constexpr (kEarlyWeights) wq_n = Rope<D>::template load_weights<kFp8>(step.q_norm_w, lq);
     tnew = ctx - 1 - t0 < split_tokens ? ctx - 1 - t0 : -1;
     if (tnew >= 0) {
+      if constexpr (kEarlyWeights) wk_n = Rope<D>::template load_weights<kFp8>(step.k_norm_w, lq);
       const size_t row = (size_t)b * num_kv_heads + h;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) knew[kk] = load16(step.k_new + row * D + 32 * kk + 8 * lq);
+      for (int kk = 0; kk < KK; ++kk)
+        knew[kk] = load16(step.k_new + row * D + Rope<D>::template dim0<kFp8>(kk, lq));
       vnew = load16(step.v_new + row * D + 8 * (lane % (D / 8)));
       slot = step.slot_mapping[b];
     }
@@ -278,20 +325,89 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   auto prologue = [&]() __attribute__((always_inline)) {
     if constexpr (kStep) {
       const Rope<D> rope(pos, lane, step.inv_scale, step.log2r);
-      rope.norm_rotate(qa, step.q_norm_w + 8 * lq, step.eps, lq);
+      rope.template norm_rotate<kFp8, kEarlyWeights>(qa, wq_n, step.q_norm_w, step.eps, lq);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         if (lr >= G) qa[kk] = u32x4{0u, 0u, 0u, 0u};  // padded rows stay zero
       if (tnew >= 0) {
-        rope.norm_rotate(knew, step.k_norm_w + 8 * lq, step.eps, lq);
-        if (slot >= 0 && slot < step.num_slots) {
-          const size_t dst = ((size_t)slot * num_kv_heads + h) * D;
-          if (lr == 0) {
+        rope.template norm_rotate<kFp8, kEarlyWeights>(knew, wk_n, step.k_norm_w, step.eps, lq);
+        pool_write = slot >= 0 && slot < step.num_slots;
+        const bool write = pool_write && !kDeferWrite;
+        const size_t dst = ((size_t)slot * num_kv_heads + h) * D;  // element offset
+        if constexpr (kFp8) {
+          // Every value of the new rows is held by several lanes; each value
+          // is divided and encoded by one of them and the codes are gathered
+          // by shuffles. K: the 16 lanes of MFMA group lq hold the same 8*KK
+          // dims (2*KK code words; code word 4m + w covers dims 64m + 16lq +
+          // 4w .. +3, i.e. BF16 words 2(w%2), +1 of knew[2m + w/2]).
+          constexpr int LPW = 16 / CW;    // lanes encoding one code word (2 or 1)
+          const int cw = lr / LPW;
+          const int kk_src = 2 * (cw / 4) + (cw % 4) / 2;
+          const int i_src = 2 * (cw % 2) + (LPW == 2 ? lr % 2 : 0);  // first BF16 word
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int k2 = 0; k2 < KK; ++k2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (k2 == kk_src && i == i_src) w0 = knew[k2][i];
+              if (k2 == kk_src && i == i_src + 1) w1 = knew[k2][i];
+            }
+          uint32_t word;
+          if constexpr (LPW == 2) {  // this lane: 2 codes, its partner the other 2
+            const uint32_t part = e4m3x2(bf16_lo(w0) / step.k_scale, bf16_hi(w0) / step.k_scale);
+            const uint32_t other = __shfl_xor(part, 1);
+            word = (lr % 2 == 0) ? (part | (other << 16)) : (other | (part << 16));
+          } else {
+            const float y[4] = {bf16_lo(w0) / step.k_scale, bf16_hi(w0) / step.k_scale,
+                                bf16_lo(w1) / step.k_scale, bf16_hi(w1) / step.k_scale};
+            word = e4m3x4(y);
+          }
+          uint32_t* codes = kcodes;
+#pragma unroll
+          for (int c2 = 0; c2 < CW; ++c2) codes[c2] = __shfl(word, (lane & 48) + c2 * LPW);
+          uint8_t* kp = static_cast<uint8_t*>(step.k_pool) + dst;
+#pragma unroll
+          for (int m = 0; m < KK / 2; ++m) {
+            if (write && lr == 0)
+              *reinterpret_cast<u32x4*>(kp + 64 * m + 16 * lq) =
+                  u32x4{codes[4 * m], codes[4 * m + 1], codes[4 * m + 2], codes[4 * m + 3]};
+            knew[2 * m] = fp8x8_to_bf16x8(codes[4 * m], codes[4 * m + 1]);
+            knew[2 * m + 1] = fp8x8_to_bf16x8(codes[4 * m + 2], codes[4 * m + 3]);
+          }
+          // V: lanes c + (D/8) k (k < NS) hold dims 8c .. 8c+7; share k
+          // encodes 8/NS of them
+          constexpr int NS = 64 / (D / 8);
+          const int vk = lane / (D / 8);
+          const int vc = lane % (D / 8);
+          uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (i == (NS == 4 ? vk : 2 * vk)) v0 = vnew[i];
+            if (i == 2 * vk + 1) v1 = vnew[i];
+          }
+          if constexpr (NS == 4) {
+            const uint32_t part = e4m3x2(bf16_lo(v0) / step.v_scale, bf16_hi(v0) / step.v_scale);
+            const uint32_t p0 = __shfl(part, vc), p1 = __shfl(part, vc + 16);
+            const uint32_t p2 = __shfl(part, vc + 32), p3 = __shfl(part, vc + 48);
+            vsub = u32x2{p0 | (p1 << 16), p2 | (p3 << 16)};
+          } else {
+            const float y[4] = {bf16_lo(v0) / step.v_scale, bf16_hi(v0) / step.v_scale,
+                                bf16_lo(v1) / step.v_scale, bf16_hi(v1) / step.v_scale};
+            const uint32_t part = e4m3x4(y);
+            vsub = u32x2{__shfl(part, vc), __shfl(part, vc + 32)};
+          }
+          if (write && lane < D / 8)
+            *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(step.v_pool) + dst + 8 * lane) = vsub;
+        } else {
+          uint16_t* kp = static_cast<uint16_t*>(step.k_pool) + dst;
+          if (write && lr == 0) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-              *reinterpret_cast<u32x4*>(step.k_pool + dst + 32 * kk + 8 * lq) = knew[kk];
+              *reinterpret_cast<u32x4*>(kp + 32 * kk + 8 * lq) = knew[kk];
           }
-          if (lane < D / 8) *reinterpret_cast<u32x4*>(step.v_pool + dst + 8 * lane) = vnew;
+          vsub = vnew;
+          if (write && lane < D / 8)
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(step.v_pool) + dst + 8 * lane) = vnew;
         }
       }
     }
@@ -337,6 +453,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
       if constexpr (kFp8) {
         const u32x4 w = buf[kk >> 1];
         kb = (kk & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+        if (new_row) kb = knew[kk];
       } else {
         kb = new_row ? knew[kk] : buf[kk];
       }
@@ -370,7 +487,6 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const int r = lane / LPR;  // token row inside a load instruction
   const int c = lane % LPR;  // 16-byte chunk of the row: dims 8c .. 8c+7
   // one lane loads the 8 values of dims 8c .. 8c+7 (16 B of BF16, 8 B of FP8)
-  using VChunk = typename std::conditional<kFp8, u32x2, u32x4>::type;
   const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 8u * ESZ * c;
   auto load_v = [&](int blk, VChunk (&buf)[PV_U]) __attribute__((always_inline)) {
     const int tl = blk * BR;
@@ -465,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
       if (tnew >= tl && tnew < tl + BR) {
 #pragma unroll
         for (int u = 0; u < PV_U; ++u)
-          if (tl + u * RPI + r == tnew) buf[u] = vnew;
+          if (tl + u * RPI + r == tnew) buf[u] = vsub;
       }
     }
 #pragma unroll
@@ -522,6 +638,33 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
           f32x4{acc[g][0] * sc, acc[g][1] * sc, acc[g][2] * sc, acc[g][3] * sc};
       *reinterpret_cast<f32x4*>(d + 4) =
           f32x4{acc[g][4] * sc, acc[g][5] * sc, acc[g][6] * sc, acc[g][7] * sc};
+    }
+  }
+
+  // the new token's rows, when their write was deferred past the wave's loads
+  if constexpr (kStep && kDeferWrite) {
+    if (tnew >= 0 && pool_write) {
+      const size_t dst = ((size_t)slot * num_kv_heads + h) * D;  // element offset
+      if constexpr (kFp8) {
+        uint8_t* kp = static_cast<uint8_t*>(step.k_pool) + dst;
+        if (lr == 0) {
+#pragma unroll
+          for (int m = 0; m < KK / 2; ++m)
+            *reinterpret_cast<u32x4*>(kp + 64 * m + 16 * lq) =
+                u32x4{kcodes[4 * m], kcodes[4 * m + 1], kcodes[4 * m + 2], kcodes[4 * m + 3]};
+        }
+        if (lane < D / 8)
+          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(step.v_pool) + dst + 8 * lane) = vsub;
+      } else {
+        uint16_t* kp = static_cast<uint16_t*>(step.k_pool) + dst;
+        if (lr == 0) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            *reinterpret_cast<u32x4*>(kp + 32 * kk + 8 * lq) = knew[kk];
+        }
+        if (lane < D / 8)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(step.v_pool) + dst + 8 * lane) = vnew;
+      }
     }
   }
 }
@@ -582,6 +725,7 @@ int launch_partition_dgt(const LaunchArgs& a) {
 
 template <int D, int G>
 int launch_partition_dg(const LaunchArgs& a) {
+  if (a.kv_fp8 && a.decode_step) return launch_partition_dgt<D, G, true, true>(a);
   if (a.kv_fp8) return launch_partition_dgt<D, G, true, false>(a);
   if (a.decode_step) return launch_partition_dgt<D, G, false, true>(a);
   return launch_partition_dgt<D, G, false, false>(a);

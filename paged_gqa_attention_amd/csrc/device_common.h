@@ -59,6 +59,48 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+// FP8 E4M3 ("FN") codes of four FP32 values, byte j from y[j]: saturated to
+// +-448 (the format has no infinity), rounded to nearest even by gfx950's
+// v_cvt_pk_fp8_f32, NaN stored as 0x7F. The explicit clamp makes the
+// conversion's own overflow handling irrelevant; NaN is set after it.
+__device__ __forceinline__ uint32_t e4m3x4(const float* y) {
+  float c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = __builtin_fminf(__builtin_fmaxf(y[j], -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  uint32_t u = (uint32_t)w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (__builtin_isnan(y[j])) u = (u & ~(0xFFu << (8 * j))) | (0x7Fu << (8 * j));
+  return u;
+}
+
+// The same encoding for two values: codes in bits 0-7 (a) and 8-15 (b).
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  const float ca = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  const float cb = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  uint32_t u = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+  if (__builtin_isnan(a)) u = (u & ~0xFFu) | 0x7Fu;
+  if (__builtin_isnan(b)) u = (u & ~0xFF00u) | 0x7F00u;
+  return u;
+}
+
+// Eight BF16 values (one 16-byte chunk) divided by `scale` (IEEE FP32
+// division) and encoded: the 8 codes of the chunk, in order.
+__device__ __forceinline__ u32x2 bf16x8_to_e4m3(u32x4 x, float scale) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    y[2 * j] = bf16_lo(x[j]) / scale;
+    y[2 * j + 1] = bf16_hi(x[j]) / scale;
+  }
+  u32x2 r;
+  r[0] = e4m3x4(y);
+  r[1] = e4m3x4(y + 4);
+  return r;
+}
+
 // Software pipeline over n items held in NB register slots (item i in slot
 // i % NB): items i+1 .. i+NB-1 are loading while item i is used. In the steady
 // state every prefetch is issued unconditionally and pinned before the use

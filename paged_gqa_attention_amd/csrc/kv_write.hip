@@ -19,13 +19,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "launch.h"
 
 namespace pa {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWriteThreads = 256;
 
@@ -45,35 +44,6 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(
   v_cache[slot * chunks_per_row + c] = vv;
 }
 
-// E4M3 codes of four FP32 values, byte j from y[j]. The explicit clamp makes
-// the conversion's own overflow handling irrelevant; NaN is set after it.
-__device__ __forceinline__ uint32_t e4m3x4(const float* y) {
-  float c[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) c[j] = __builtin_fminf(__builtin_fmaxf(y[j], -448.0f), 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
-  uint32_t u = (uint32_t)w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (__builtin_isnan(y[j])) u = (u & ~(0xFFu << (8 * j))) | (0x7Fu << (8 * j));
-  return u;
-}
-
-// Eight BF16 values (one 16-byte chunk) divided by `scale` and encoded.
-__device__ __forceinline__ u32x2 quantize8(u32x4 x, float scale) {
-  float y[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    y[2 * j] = __uint_as_float(x[j] << 16) / scale;
-    y[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u) / scale;
-  }
-  u32x2 r;
-  r[0] = e4m3x4(y);
-  r[1] = e4m3x4(y + 4);
-  return r;
-}
-
 __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
     const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
     const int32_t* __restrict__ slot_mapping, u32x2* __restrict__ k_codes,
@@ -87,8 +57,8 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
   if (slot < 0 || slot >= num_slots) return;  // padding token / outside the pool
   const u32x4 kv = k_new[i];
   const u32x4 vv = v_new[i];
-  k_codes[slot * chunks_per_row + c] = quantize8(kv, k_scale);
-  v_codes[slot * chunks_per_row + c] = quantize8(vv, v_scale);
+  k_codes[slot * chunks_per_row + c] = bf16x8_to_e4m3(kv, k_scale);
+  v_codes[slot * chunks_per_row + c] = bf16x8_to_e4m3(vv, v_scale);
 }
 
 }  // namespace

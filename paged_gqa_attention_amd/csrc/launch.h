@@ -17,9 +17,10 @@ struct DecodeStepArgs {
   const uint16_t* k_norm_w;   // bf16 [D]
   const int32_t* positions;   // int32 [B]: RoPE position of the new token
   const int32_t* slot_mapping;// int32 [B]: pool slot of the new token; outside the pool: not written
-  uint16_t* k_pool;           // bf16 [N, P, Hkv, D], written at the new token's slot
-  uint16_t* v_pool;
+  void* k_pool;               // bf16 or fp8-e4m3 [N, P, Hkv, D], written at the new token's slot
+  void* v_pool;
   long long num_slots;        // N * P
+  float k_scale, v_scale;     // fp8 pools: the new rows are stored as codes of x / scale
   float eps;                  // RMSNorm epsilon
   double inv_scale;           // 1 / rope_scale
   double log2r;               // -2 * log2(rope_base) / D
@@ -125,10 +126,12 @@ struct PrologueArgs {
   const int32_t* positions;    // int32 [T]
   const int32_t* slot_mapping; // int32 [T]
   uint16_t* q_out;             // bf16 [T, Hq, D] (may equal q_in)
-  uint16_t* k_cache;           // bf16 [N, P, Hkv, D]
-  uint16_t* v_cache;           // bf16 [N, P, Hkv, D]
+  void* k_cache;               // bf16 [N, P, Hkv, D], or E4M3 codes when fp8
+  void* v_cache;               // bf16 [N, P, Hkv, D], or E4M3 codes when fp8
   int num_tokens, num_q_heads, num_kv_heads, head_dim, page_size, num_pages;
   float eps, rope_base, rope_scale;
+  bool fp8 = false;            // store codes of x / k_scale, x / v_scale
+  float k_scale = 1.0f, v_scale = 1.0f;
   void* stream;                // hipStream_t
 };
 

@@ -22,6 +22,12 @@
 // butterfly (same value and order on every lane), and the RoPE partner values
 // come from the lane D/16 away by a shuffle. HBM-bound: every byte is read once
 // and written once.
+//
+// kFp8: the pools hold FP8 E4M3 codes with one FP32 scale each. The K row is
+// first rounded to BF16 exactly as for BF16 pools, then each value is divided
+// by k_scale and encoded (saturating, nearest even), as pa_kv_write_fp8 stores
+// a BF16 row; V is encoded from its BF16 input with v_scale. The result is
+// the BF16 prologue followed by the FP8 KV write, in one pass.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -35,19 +41,26 @@ namespace {
 
 constexpr int kProThreads = 256;
 
-template <int D>
+template <int D, bool kFp8>
 __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     const uint16_t* q_in, const uint16_t* __restrict__ k_in,
     const uint16_t* __restrict__ v_in, const uint16_t* __restrict__ q_norm_w,
     const uint16_t* __restrict__ k_norm_w, const int32_t* __restrict__ positions,
-    const int32_t* __restrict__ slot_mapping, uint16_t* q_out, uint16_t* __restrict__ k_cache,
-    uint16_t* __restrict__ v_cache, int num_q_heads, int num_kv_heads, long long num_slots,
-    float eps, double log2_base, double inv_scale) {
+    const int32_t* __restrict__ slot_mapping, uint16_t* q_out, void* __restrict__ k_cache,
+    void* __restrict__ v_cache, int num_q_heads, int num_kv_heads, long long num_slots,
+    float eps, double log2_base, double inv_scale, float k_scale, float v_scale) {
   constexpr int LPR = D / 8;              // lanes per head row
   constexpr int RPP = kProThreads / LPR;  // rows per pass
   constexpr int H = D / 2;
   __shared__ float s_cos[H];
   __shared__ float s_sin[H];
+  // 8 BF16 values at element offset e of a pool: copied, or encoded to FP8
+  auto store_row_chunk = [](void* pool, size_t e, u32x4 x, float scale) {
+    if constexpr (kFp8)
+      *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(pool) + e) = bf16x8_to_e4m3(x, scale);
+    else
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(pool) + e) = x;
+  };
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -76,8 +89,8 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     const uint16_t* src = is_q ? q_in + ((size_t)t * num_q_heads + h) * D
                                : (is_k ? k_in : v_in) + ((size_t)t * num_kv_heads + h) * D;
     const u32x4 xw = load16(src + 8 * c);
-    if (!is_q && !is_k) {  // V: a plain copy into its slot
-      if (write_kv) *reinterpret_cast<u32x4*>(v_cache + (kv_row + h) * D + 8 * c) = xw;
+    if (!is_q && !is_k) {  // V: a plain copy (or its codes) into its slot
+      if (write_kv) store_row_chunk(v_cache, (kv_row + h) * D + 8 * c, xw, v_scale);
       continue;
     }
     float x[8];
@@ -117,12 +130,12 @@ __global__ __launch_bounds__(kProThreads) void prologue_kernel(
     if (is_q) {
       *reinterpret_cast<u32x4*>(q_out + ((size_t)t * num_q_heads + h) * D + 8 * c) = ow;
     } else if (write_kv) {
-      *reinterpret_cast<u32x4*>(k_cache + (kv_row + h) * D + 8 * c) = ow;
+      store_row_chunk(k_cache, (kv_row + h) * D + 8 * c, ow, k_scale);
     }
   }
 }
 
-template <int D>
+template <int D, bool kFp8>
 int launch_prologue_d(const PrologueArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const long long num_slots = (long long)a.num_pages * a.page_size;
@@ -133,15 +146,17 @@ int launch_prologue_d(const PrologueArgs& a) {
                   (void*)&a.slot_mapping, (void*)&a.q_out,     (void*)&a.k_cache,
                   (void*)&a.v_cache,    (void*)&a.num_q_heads, (void*)&a.num_kv_heads,
                   (void*)&num_slots,    (void*)&a.eps,
-                  (void*)&log2_base,    (void*)&inv_scale};
-  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&prologue_kernel<D>),
+                  (void*)&log2_base,    (void*)&inv_scale, (void*)&a.k_scale,
+                  (void*)&a.v_scale};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(&prologue_kernel<D, kFp8>),
                               dim3(a.num_tokens), dim3(kProThreads), args, 0, stream);
 }
 
 }  // namespace
 
 int launch_prologue(const PrologueArgs& a) {
-  return a.head_dim == 128 ? launch_prologue_d<128>(a) : launch_prologue_d<256>(a);
+  if (a.fp8) return a.head_dim == 128 ? launch_prologue_d<128, true>(a) : launch_prologue_d<256, true>(a);
+  return a.head_dim == 128 ? launch_prologue_d<128, false>(a) : launch_prologue_d<256, false>(a);
 }
 
 }  // namespace pa

@@ -9,7 +9,8 @@ the library is missing, importing the binding raises instead of falling back.
 Names follow the C ABI: ``pa_decode``, ``pa_decode_fp8``, ``pa_decode_step``, ``pa_plan``,
 ``pa_workspace_size``, ``pa_decode_partials``, ``pa_merge_partials``,
 ``pa_kv_write``, ``pa_kv_write_fp8``, ``pa_mq_plan``, ``pa_mq_attention``, ``pa_mq_attention_fp8``,
-``pa_attention_prologue``, ``pa_status_string``, ``pa_abi_version``.
+``pa_attention_prologue``, ``pa_attention_prologue_fp8``, ``pa_decode_step_fp8``,
+``pa_status_string``, ``pa_abi_version``.
 """
 
 from __future__ import annotations
@@ -166,6 +167,21 @@ def _load():
         ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p,
     ]
+    lib.pa_attention_prologue_fp8.restype = ctypes.c_int
+    lib.pa_attention_prologue_fp8.argtypes = [
+        ctypes.POINTER(PaPrologueShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.pa_decode_step_fp8.restype = ctypes.c_int
+    lib.pa_decode_step_fp8.argtypes = [
+        ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
     lib.pa_decode_step.restype = ctypes.c_int
     lib.pa_decode_step.argtypes = [
         ctypes.POINTER(PaShape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -230,7 +246,7 @@ def shape_of(q, k_cache, block_table, split_pages: int = 0) -> PaShape:
     return make_shape(B, Hq, Hkv, D, block_table.shape[1], N, P, split_pages)
 
 
-def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
+def _check_inputs(q, k_cache, v_cache, block_table, context_lens, cache_dtype=torch.bfloat16):
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("expected q [B,Hq,D] and k_cache == v_cache shape [N,P,Hkv,D]")
     B, Hq, D = q.shape
@@ -238,8 +254,8 @@ def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
         raise ValueError("head_dim of q and of the caches differ")
     if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("expected block_table [B, W] and context_lens [B]")
-    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, torch.bfloat16),
-                        ("v_cache", v_cache, torch.bfloat16),
+    for name, t, dt in (("q", q, torch.bfloat16), ("k_cache", k_cache, cache_dtype),
+                        ("v_cache", v_cache, cache_dtype),
                         ("block_table", block_table, torch.int32),
                         ("context_lens", context_lens, torch.int32)):
         if t.dtype != dt:
@@ -292,24 +308,12 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
-def pa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                   q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
-                   positions: torch.Tensor, slot_mapping: torch.Tensor,
-                   k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
-                   context_lens: torch.Tensor, scale: Optional[float] = None,
-                   eps: float = 1e-6, rope_base: float = 1e6, rope_scale: float = 1.0,
-                   out: Optional[torch.Tensor] = None, split_pages: int = 0,
-                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """A decode step's attention with its prologue fused in; returns ``out``.
-
-    q [B, Hq, D] is the projection's q (before QK-norm and RoPE); k_new and
-    v_new [B, Hkv, D] the new token's K and V; sequence b's new token is token
-    context_lens[b] - 1, rotated at positions[b] and written to
-    slot_mapping[b] of the pools (updated in place), then decode attention over
-    the context follows. Other arguments as for ``pa_decode`` and
-    ``pa_attention_prologue``.
-    """
-    _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+def _decode_step(q, k_new, v_new, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                 k_cache, v_cache, block_table, context_lens, scale, eps, rope_base, rope_scale,
+                 out, split_pages, workspace, fp8_scales):
+    fp8 = fp8_scales is not None
+    _check_inputs(q, k_cache, v_cache, block_table, context_lens,
+                  torch.uint8 if fp8 else torch.bfloat16)
     B, Hq, D = q.shape
     Hkv = k_cache.shape[2]
     for name, t, shp, dt in (("k_new", k_new, (B, Hkv, D), torch.bfloat16),
@@ -333,17 +337,59 @@ def pa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     need = pa_workspace_size(shape)
     if workspace is None:
         workspace = _workspace(q.device, need)
-    st = _lib.pa_decode_step(ctypes.byref(shape), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-                             q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
-                             positions.data_ptr(), slot_mapping.data_ptr(), ctypes.c_float(eps),
-                             ctypes.c_float(rope_base), ctypes.c_float(rope_scale),
-                             k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-                             context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
-                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             _stream(q.device))
+    head = (ctypes.byref(shape), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+            q_norm_weight.data_ptr(), k_norm_weight.data_ptr(), positions.data_ptr(),
+            slot_mapping.data_ptr(), ctypes.c_float(eps), ctypes.c_float(rope_base),
+            ctypes.c_float(rope_scale))
+    tail = (k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+            context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    if fp8:
+        st = _lib.pa_decode_step_fp8(*head, ctypes.c_float(fp8_scales[0]),
+                                     ctypes.c_float(fp8_scales[1]), *tail)
+    else:
+        st = _lib.pa_decode_step(*head, *tail)
     if st != PA_OK:
-        raise PagedAttnError(st, "pa_decode_step")
+        raise PagedAttnError(st, "pa_decode_step_fp8" if fp8 else "pa_decode_step")
     return out
+
+
+def pa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                   positions: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   context_lens: torch.Tensor, scale: Optional[float] = None,
+                   eps: float = 1e-6, rope_base: float = 1e6, rope_scale: float = 1.0,
+                   out: Optional[torch.Tensor] = None, split_pages: int = 0,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A decode step's attention with its prologue fused in; returns ``out``.
+
+    q [B, Hq, D] is the projection's q (before QK-norm and RoPE); k_new and
+    v_new [B, Hkv, D] the new token's K and V; sequence b's new token is token
+    context_lens[b] - 1, rotated at positions[b] and written to
+    slot_mapping[b] of the pools (updated in place), then decode attention over
+    the context follows. Other arguments as for ``pa_decode`` and
+    ``pa_attention_prologue``.
+    """
+    return _decode_step(q, k_new, v_new, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                        k_cache, v_cache, block_table, context_lens, scale, eps, rope_base,
+                        rope_scale, out, split_pages, workspace, None)
+
+
+def pa_decode_step_fp8(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                       positions: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                       v_scale: float, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                       block_table: torch.Tensor, context_lens: torch.Tensor,
+                       scale: Optional[float] = None, eps: float = 1e-6, rope_base: float = 1e6,
+                       rope_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                       split_pages: int = 0,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``pa_decode_step`` over FP8-E4M3 pools (uint8 codes, values code * scale):
+    the new K (BF16 after norm and RoPE) and V are written as codes of x / scale."""
+    return _decode_step(q, k_new, v_new, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                        k_codes, v_codes, block_table, context_lens, scale, eps, rope_base,
+                        rope_scale, out, split_pages, workspace, (k_scale, v_scale))
 
 
 def pa_decode_fp8(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
@@ -562,18 +608,10 @@ def pa_mq_attention_fp8(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.T
                scale, out, split_pages, workspace, True, k_scale, v_scale)
 
 
-def pa_attention_prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                          q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
-                          positions: torch.Tensor, slot_mapping: torch.Tensor,
-                          k_cache: torch.Tensor, v_cache: torch.Tensor, eps: float = 1e-6,
-                          rope_base: float = 1e6, rope_scale: float = 1.0,
-                          q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """QK-norm + NeoX RoPE + KV write of T new tokens; returns q_out [T, Hq, D].
-
-    q [T, Hq, D], k and v [T, Hkv, D], weights [D] (all bf16), positions and
-    slot_mapping [T] int32; k_cache / v_cache [N, 128, Hkv, D] bf16 are
-    updated in place (K after norm and RoPE, V as given).
-    """
+def _prologue(q, k, v, q_norm_weight, k_norm_weight, positions, slot_mapping, k_cache, v_cache,
+              eps, rope_base, rope_scale, q_out, fp8_scales):
+    fp8 = fp8_scales is not None
+    cache_dt = torch.uint8 if fp8 else torch.bfloat16
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k_cache.dim() != 4 \
             or v_cache.shape != k_cache.shape:
         raise ValueError("expected q [T,Hq,D], k == v shape [T,Hkv,D], caches [N,P,Hkv,D]")
@@ -589,7 +627,7 @@ def pa_attention_prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         ("k_norm_weight", k_norm_weight, torch.bfloat16),
                         ("positions", positions, torch.int32),
                         ("slot_mapping", slot_mapping, torch.int32),
-                        ("k_cache", k_cache, torch.bfloat16), ("v_cache", v_cache, torch.bfloat16)):
+                        ("k_cache", k_cache, cache_dt), ("v_cache", v_cache, cache_dt)):
         if t.dtype != dt:
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
         if not t.is_contiguous():
@@ -601,12 +639,45 @@ def pa_attention_prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check_out(q_out, q)
     shape = PaPrologueShape(int(T), int(Hq), int(k.shape[1]), int(D), int(k_cache.shape[1]),
                             int(k_cache.shape[0]))
-    st = _lib.pa_attention_prologue(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                    q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
-                                    positions.data_ptr(), slot_mapping.data_ptr(),
-                                    ctypes.c_float(eps), ctypes.c_float(rope_base),
-                                    ctypes.c_float(rope_scale), q_out.data_ptr(),
-                                    k_cache.data_ptr(), v_cache.data_ptr(), _stream(q.device))
+    head = (ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            q_norm_weight.data_ptr(), k_norm_weight.data_ptr(), positions.data_ptr(),
+            slot_mapping.data_ptr(), ctypes.c_float(eps), ctypes.c_float(rope_base),
+            ctypes.c_float(rope_scale))
+    tail = (q_out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), _stream(q.device))
+    if fp8:
+        st = _lib.pa_attention_prologue_fp8(*head, ctypes.c_float(fp8_scales[0]),
+                                            ctypes.c_float(fp8_scales[1]), *tail)
+    else:
+        st = _lib.pa_attention_prologue(*head, *tail)
     if st != PA_OK:
-        raise PagedAttnError(st, "pa_attention_prologue")
+        raise PagedAttnError(st, "pa_attention_prologue_fp8" if fp8 else "pa_attention_prologue")
     return q_out
+
+
+def pa_attention_prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                          positions: torch.Tensor, slot_mapping: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor, eps: float = 1e-6,
+                          rope_base: float = 1e6, rope_scale: float = 1.0,
+                          q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """QK-norm + NeoX RoPE + KV write of T new tokens; returns q_out [T, Hq, D].
+
+    q [T, Hq, D], k and v [T, Hkv, D], weights [D] (all bf16), positions and
+    slot_mapping [T] int32; k_cache / v_cache [N, 128, Hkv, D] bf16 are
+    updated in place (K after norm and RoPE, V as given).
+    """
+    return _prologue(q, k, v, q_norm_weight, k_norm_weight, positions, slot_mapping, k_cache,
+                     v_cache, eps, rope_base, rope_scale, q_out, None)
+
+
+def pa_attention_prologue_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor,
+                              positions: torch.Tensor, slot_mapping: torch.Tensor,
+                              k_scale: float, v_scale: float, k_codes: torch.Tensor,
+                              v_codes: torch.Tensor, eps: float = 1e-6, rope_base: float = 1e6,
+                              rope_scale: float = 1.0,
+                              q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``pa_attention_prologue`` writing FP8-E4M3 pools (uint8 codes of the BF16
+    K row / k_scale and v / v_scale); returns q_out [T, Hq, D]."""
+    return _prologue(q, k, v, q_norm_weight, k_norm_weight, positions, slot_mapping, k_codes,
+                     v_codes, eps, rope_base, rope_scale, q_out, (k_scale, v_scale))

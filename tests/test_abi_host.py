@@ -34,8 +34,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert names == ["pa_abi_version", "pa_attention_prologue", "pa_decode", "pa_decode_fp8",
-                     "pa_decode_partials", "pa_decode_step", "pa_kv_write", "pa_kv_write_fp8",
+    assert names == ["pa_abi_version", "pa_attention_prologue", "pa_attention_prologue_fp8",
+                     "pa_decode", "pa_decode_fp8", "pa_decode_partials", "pa_decode_step",
+                     "pa_decode_step_fp8", "pa_kv_write", "pa_kv_write_fp8",
                      "pa_merge_partials", "pa_mq_attention",
                      "pa_mq_attention_fp8", "pa_mq_plan", "pa_plan", "pa_status_string",
                      "pa_workspace_size"]
@@ -432,3 +433,33 @@ def test_decode_step_rejects_bad_arguments():
     s0 = pa.make_shape(0, 40, 8, 128, 32, 64)
     assert pa.lib.pa_decode_step(ctypes.byref(s0), *([None] * 7 + ok[7:10] + [None] * 4 +
                                                      [ok[14], None, None, 0, None])) == pa.PA_OK
+
+
+@fake_pointers
+def test_fp8_prologue_and_step_reject_bad_scales():
+    # the FP8 variants: the BF16 entry points' checks plus finite positive scales
+    d = 1 << 20
+    f = ctypes.c_float
+    ps = pa.PaPrologueShape(16, 40, 8, 128, 128, 512)
+    pro = lambda ks, vs, tail: pa.lib.pa_attention_prologue_fp8(
+        ctypes.byref(ps), *([d] * 7 + [f(1e-6), f(1e6), f(1.0), f(ks), f(vs)] + tail))
+    s = pa.make_shape(2, 40, 8, 128, 32, 64)
+    need = pa.pa_workspace_size(s)
+    step = lambda ks, vs, tail: pa.lib.pa_decode_step_fp8(
+        ctypes.byref(s), *([d] * 7 + [f(1e-6), f(1e6), f(1.0), f(ks), f(vs)] + tail))
+    step_tail = [d, d, d, d, f(0.1), d, d, need, None]
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        assert pro(ks, vs, [d, d, d, None]) == pa.PA_ERR_INVALID_ARGUMENT, (ks, vs)
+        assert step(ks, vs, step_tail) == pa.PA_ERR_INVALID_ARGUMENT, (ks, vs)
+    # pointer and alignment checks of the codes pools
+    assert pro(0.5, 0.5, [d, None, d, None]) == pa.PA_ERR_NULL_POINTER
+    assert pro(0.5, 0.5, [d, d, d + 8, None]) == pa.PA_ERR_INVALID_ARGUMENT
+    assert step(0.5, 0.5, [None] + step_tail[1:]) == pa.PA_ERR_NULL_POINTER
+    assert step(0.5, 0.5, [d + 8] + step_tail[1:]) == pa.PA_ERR_INVALID_ARGUMENT
+    t = list(step_tail)
+    t[7] = need - 1
+    assert step(0.5, 0.5, t) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    ps0 = pa.PaPrologueShape(0, 40, 8, 128, 128, 512)
+    assert pa.lib.pa_attention_prologue_fp8(
+        ctypes.byref(ps0), *([None] * 7 + [f(1e-6), f(1e6), f(1.0), f(0.5), f(0.5)] +
+                             [None] * 4)) == pa.PA_OK

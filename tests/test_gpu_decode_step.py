@@ -158,3 +158,115 @@ def test_decode_step_matches_separate_prologue_and_decode():
     assert torch.equal(vcf.view(torch.int16), vc.cpu().view(torch.int16))
     kd = (kcf.float() - kc.cpu().float()).abs()
     assert float(kd.max()) <= 2.0 ** -7 * float(kc.cpu().float().abs().max())
+
+
+# ---- FP8-E4M3 pools (pa_decode_step_fp8) -----------------------------------------
+# The new token's K (BF16 after norm and RoPE) and V are written as codes;
+# attention reads the codes. Reference: the oracle's FP8 prologue (codes of the
+# BF16-rounded FP64 K row) and its FP8 decode over the codes it wrote. The
+# kernel's BF16 K row may differ from the oracle's by one BF16 step, so single
+# K codes may differ by one E4M3 step: K codes are gated against the FP64 row
+# (half a step, as for pa_attention_prologue_fp8), the attention output by the
+# usual gate; V codes and untouched rows are bit-exact. K values past
+# 448 * k_scale saturate (the reference is clipped there).
+
+def run_step_fp8(w, x, f, split_pages=0, eps=1e-6, base=1e6, rscale=1.0):
+    from paged_gqa_attention_amd import pagedattn as pa
+    kc, vc = f.k_codes.to(DEV), f.v_codes.to(DEV)
+    out = pa.pa_decode_step_fp8(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["wq"].to(DEV),
+                                x["wk"].to(DEV), x["pos"].to(DEV), x["slots"].to(DEV), f.k_scale,
+                                f.v_scale, kc, vc, w.block_table.to(DEV), w.context_lens.to(DEV),
+                                scale=w.scale, eps=eps, rope_base=base, rope_scale=rscale,
+                                split_pages=split_pages)
+    torch.cuda.synchronize()
+    return out.cpu(), kc.cpu(), vc.cpu()
+
+
+def reference_fp8(w, x, f, eps=1e-6, base=1e6, rscale=1.0):
+    rq, rk8, rv8 = oracle.attention_prologue_fp8(
+        x["q"], x["k"], x["v"], x["wq"], x["wk"], x["pos"], x["slots"], np.float32(eps),
+        np.float32(base), np.float32(rscale), np.float32(f.k_scale), np.float32(f.v_scale),
+        f.k_codes.numpy(), f.v_codes.numpy())
+    q16 = torch.from_numpy(rq).to(torch.bfloat16)
+    out = oracle.paged_decode_attention_fp8(q16, rk8, rv8, f.k_scale, f.v_scale, w.block_table,
+                                            w.context_lens, w.scale)
+    return out, rk8, rv8
+
+
+def check_pools_fp8(w, x, f, kc, vc, rv8, what, eps=1e-6, base=1e6, rscale=1.0):
+    N = w.k_cache.shape[0]
+    written = np.zeros((N, 128), bool)
+    for s in x["slots"].tolist():
+        if 0 <= s < N * 128:
+            written[s // 128, s % 128] = True
+    assert np.array_equal(vc.numpy(), rv8), f"{what}: V codes"
+    assert np.array_equal(kc.numpy()[~written], f.k_codes.numpy()[~written]), f"{what}: K rows"
+    _, rk64, _ = oracle.attention_prologue(x["q"], x["k"], x["v"], x["wq"], x["wk"], x["pos"],
+                                           x["slots"], np.float32(eps), np.float32(base),
+                                           np.float32(rscale), w.k_cache, w.v_cache)
+    lim = 448.0 * float(np.float32(f.k_scale))           # codes saturate at +-448
+    ref = np.clip(rk64[written], -lim, lim)
+    dec = oracle.decode_fp8_e4m3(kc.numpy()[written]) * float(np.float32(f.k_scale))
+    bound = (2.0 ** -4 + 2.0 ** -8) * np.abs(ref) * 1.001 + 2.0 ** -10 * f.k_scale + 1e-4
+    assert np.all(np.abs(dec - ref) <= bound), f"{what}: new K codes"
+
+
+@pytest.mark.parametrize("split_pages", [0, 1])
+def test_decode_step_fp8_qwen_shape(split_pages):
+    announce(f"decode step fp8 40/8/128 sp{split_pages}")
+    ctx = [1, 130, 1000, 4096, 129, 2048]
+    w, x = make_step(len(ctx), 40, 8, 128, ctx, seed=41, W=32)
+    f = workloads.quantize_fp8(w)
+    out, kc, vc = run_step_fp8(w, x, f, split_pages)
+    ref, rk8, rv8 = reference_fp8(w, x, f)
+    assert_parity(out, ref, f"decode step fp8 sp{split_pages}")
+    check_pools_fp8(w, x, f, kc, vc, rv8, "decode step fp8")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 2, 256), (8, 8, 128), (3, 1, 256)])
+def test_decode_step_fp8_head_shapes(Hq, Hkv, D):
+    announce(f"decode step fp8 {Hq}/{Hkv}/{D}")
+    ctx = [17, 300, 777]
+    w, x = make_step(len(ctx), Hq, Hkv, D, ctx, seed=Hq + D + 3, W=8)
+    f = workloads.quantize_fp8(w)
+    out, kc, vc = run_step_fp8(w, x, f)
+    ref, rk8, rv8 = reference_fp8(w, x, f)
+    assert_parity(out, ref, f"decode step fp8 {Hq}/{Hkv}/{D}")
+    check_pools_fp8(w, x, f, kc, vc, rv8, f"decode step fp8 {Hq}/{Hkv}/{D}")
+
+
+def test_decode_step_fp8_parameters_and_empty_context():
+    announce("decode step fp8 parameters, ctx 0")
+    ctx = [0, 200, 1000, 3000]
+    pos = [0, 123456789, 4095, (1 << 27) - 1]
+    w, x = make_step(len(ctx), 40, 8, 128, ctx, seed=43, W=24, positions=pos)
+    f = workloads.quantize_fp8(w)
+    out, kc, vc = run_step_fp8(w, x, f, eps=1e-5, base=1e4, rscale=4.0)
+    ref, rk8, rv8 = reference_fp8(w, x, f, eps=1e-5, base=1e4, rscale=4.0)
+    assert torch.all(out[0] == 0)
+    assert_parity(out, ref, "decode step fp8 params")
+    check_pools_fp8(w, x, f, kc, vc, rv8, "decode step fp8 params", eps=1e-5, base=1e4, rscale=4.0)
+
+
+def test_decode_step_fp8_matches_separate_kernels():
+    # against pa_attention_prologue_fp8 then pa_decode_fp8 on the GPU
+    from paged_gqa_attention_amd import pagedattn as pa
+    announce("decode step fp8 vs separate kernels")
+    ctx = [1, 257, 4096, 1500]
+    w, x = make_step(len(ctx), 40, 8, 128, ctx, seed=45, W=32)
+    f = workloads.quantize_fp8(w)
+    fused, kcf, vcf = run_step_fp8(w, x, f)
+    kc, vc = f.k_codes.to(DEV), f.v_codes.to(DEV)
+    qo = pa.pa_attention_prologue_fp8(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV),
+                                      x["wq"].to(DEV), x["wk"].to(DEV), x["pos"].to(DEV),
+                                      x["slots"].to(DEV), f.k_scale, f.v_scale, kc, vc)
+    sep = pa.pa_decode_fp8(qo, kc, vc, f.k_scale, f.v_scale, w.block_table.to(DEV),
+                           w.context_lens.to(DEV), scale=w.scale).cpu()
+    torch.cuda.synchronize()
+    d = (fused.float() - sep.float()).abs()
+    announce(f"  fused vs separate: max-abs {float(d.max()):.3e}")
+    assert float(d.max()) <= 2e-2 and float(d.mean()) <= 2e-3
+    assert torch.equal(vcf, vc.cpu())
+    a = oracle.decode_fp8_e4m3(kcf.numpy())
+    b = oracle.decode_fp8_e4m3(kc.cpu().numpy())
+    assert np.all(np.abs(a - b) <= 2.0 ** -3 * np.maximum(np.abs(a), np.abs(b)) + 2.0 ** -9)

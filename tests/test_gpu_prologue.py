@@ -188,3 +188,89 @@ def test_decode_step_end_to_end():
     assert_close(qo.cpu(), rq, "e2e q")
     ref = oracle.paged_decode_attention(rq16, rk16, rv16, bt, w.context_lens, w.scale)
     assert_parity(out.cpu(), ref, "prologue + decode")
+
+
+# ---- FP8-E4M3 pools ------------------------------------------------------------
+# K codes: the kernel's BF16 K row (within the gate above of the FP64 row)
+# divided by k_scale and encoded, so the decoded value is within half an E4M3
+# step (2^-4 relative, 2^-10 * k_scale absolute below the normal range) of that
+# row: gate |code * k_scale - K_oracle| <= (2^-4 + 2^-8)|K| * 1.001 + 2^-10 k_scale
+# + 1e-4. V codes: bit-exact (the division and encoding of the BF16 input are
+# fixed). The K codes also equal pa_kv_write_fp8 of the BF16 prologue's own K
+# rows, bit for bit (same rounding to BF16, same encoder).
+
+def run_gpu_fp8(x, ks, vs, kc8, vc8, eps=1e-6, base=1e6, scale=1.0):
+    from paged_gqa_attention_amd import pagedattn as pa
+    g = {n: t.to(DEV) for n, t in x.items()}
+    k8, v8 = kc8.to(DEV), vc8.to(DEV)
+    qo = pa.pa_attention_prologue_fp8(g["q"], g["k"], g["v"], g["wq"], g["wk"], g["pos"],
+                                      g["slots"], ks, vs, k8, v8, eps=eps, rope_base=base,
+                                      rope_scale=scale)
+    torch.cuda.synchronize()
+    return qo.cpu(), k8.cpu(), v8.cpu()
+
+
+def check_fp8(x, ks, vs, what, eps=1e-6, base=1e6, scale=1.0):
+    from paged_gqa_attention_amd import pagedattn as pa
+    N, P, Hkv, D = x["kc"].shape
+    gen = torch.Generator().manual_seed(5)
+    kc8 = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, dtype=torch.uint8)
+    vc8 = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, dtype=torch.uint8)
+    qo, k8, v8 = run_gpu_fp8(x, ks, vs, kc8, vc8, eps, base, scale)
+    rq, rk8, rv8 = oracle.attention_prologue_fp8(
+        x["q"], x["k"], x["v"], x["wq"], x["wk"], x["pos"], x["slots"], np.float32(eps),
+        np.float32(base), np.float32(scale), np.float32(ks), np.float32(vs), kc8.numpy(),
+        vc8.numpy())
+    assert_close(qo, rq, f"{what} q")
+    written = np.zeros((N, P), bool)
+    for s in x["slots"].tolist():
+        if 0 <= s < N * P:
+            written[s // P, s % P] = True
+    assert np.array_equal(v8.numpy(), rv8), f"{what} V codes"
+    assert np.array_equal(k8.numpy()[~written], kc8.numpy()[~written]), f"{what} untouched K"
+    # K against the FP64 rotated rows (the oracle's BF16 prologue, unrounded)
+    _, rk64, _ = run_oracle(x, eps, base, scale)
+    dec = oracle.decode_fp8_e4m3(k8.numpy()[written]) * float(np.float32(ks))
+    lim = 448.0 * float(np.float32(ks))                   # codes saturate at +-448
+    ref = np.clip(rk64[written], -lim, lim)
+    bound = (2.0 ** -4 + 2.0 ** -8) * np.abs(ref) * 1.001 + 2.0 ** -10 * ks + 1e-4
+    err = np.abs(dec - ref)
+    announce(f"{what} K codes: worst err/bound {float(np.max(err / bound)):.3f}, "
+             f"{float(np.mean(k8.numpy()[written] == rk8[written])):.5f} equal to the oracle's")
+    assert np.all(err <= bound), f"{what} K codes"
+    # the same bits as the BF16 prologue followed by the FP8 KV write
+    g = {n: t.to(DEV) for n, t in x.items()}
+    pa.pa_attention_prologue(g["q"], g["k"], g["v"], g["wq"], g["wk"], g["pos"], g["slots"],
+                             g["kc"], g["vc"], eps=eps, rope_base=base, rope_scale=scale)
+    k16 = torch.stack([g["kc"][s // P, s % P] for s in x["slots"].tolist() if 0 <= s < N * P]) \
+        if written.any() else None
+    if k16 is not None:
+        sl = torch.tensor([s for s in x["slots"].tolist() if 0 <= s < N * P], dtype=torch.int32)
+        k8b, v8b = kc8.to(DEV), vc8.to(DEV)
+        vrows = torch.stack([x["v"][t] for t, s in enumerate(x["slots"].tolist())
+                             if 0 <= s < N * P]).to(DEV)
+        pa.pa_kv_write_fp8(k16.contiguous(), vrows.contiguous(), ks, vs, sl.to(DEV), k8b, v8b)
+        torch.cuda.synchronize()
+        assert torch.equal(k8b.cpu(), k8), f"{what}: prologue_fp8 != prologue + kv_write_fp8"
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,ks", [(40, 8, 128, 0.05), (16, 2, 256, 0.02), (8, 8, 128, 1.0)])
+def test_fp8_prologue(Hq, Hkv, D, ks):
+    announce(f"fp8 prologue {Hq}/{Hkv}/{D} k_scale {ks}")
+    x = make_inputs(300, Hq, Hkv, D, 8, seed=Hq + D + 7)
+    check_fp8(x, ks, 0.0137, f"fp8 prologue {Hq}/{Hkv}/{D}")
+
+
+def test_fp8_prologue_padding_saturation_and_parameters():
+    # padding and out-of-pool slots write nothing; a tiny k_scale saturates K
+    # codes at +-448 (the bound then does not hold: checked separately)
+    announce("fp8 prologue padding / parameters")
+    x = make_inputs(20, 40, 8, 128, 4, seed=77, slots=[5, -1, 4 * 128, 7, -9] + list(range(8, 23)),
+                    positions=[(1 << 27) - 1] + list(range(19)))
+    check_fp8(x, 0.05, 0.02, "fp8 prologue params", eps=1e-5, base=1e4, scale=4.0)
+    from paged_gqa_attention_amd import pagedattn as pa
+    kc8 = torch.zeros(4, 128, 8, 128, dtype=torch.uint8)
+    qo, k8, v8 = run_gpu_fp8(x, 1e-4, 1e-4, kc8, kc8.clone())
+    codes = k8[0, 5].numpy()
+    assert set(np.unique(codes & 0x7F).tolist()) <= set(range(0x7F))   # never NaN
+    assert np.mean((codes & 0x7F) == 0x7E) > 0.9                        # saturated

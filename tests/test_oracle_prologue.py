@@ -106,6 +106,51 @@ def test_prologue_writes_normed_rotated_k_and_raw_v():
     assert np.array_equal(vc2[~touched], vc[~touched])
 
 
+def test_round_bf16_matches_torch_and_ties_to_even():
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal(100000) * np.exp2(rng.integers(-140, 120, 100000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()   # one rounding from FP32
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+    got = oracle.round_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8),
+                                      1 + 2.0 ** -8 + 2.0 ** -40, 0.0]))
+    assert got.tolist() == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7, 0.0]
+
+
+def test_fp8_prologue_writes_codes_of_the_bf16_rows():
+    T, Hq, Hkv, D, N, P = 6, 4, 2, 128, 3, 128
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hkv, D))
+    v = torch.from_numpy(rng.standard_normal((T, Hkv, D))).to(torch.bfloat16)
+    wq, wk = rng.standard_normal(D), rng.standard_normal(D)
+    kc = rng.integers(0, 256, (N, P, Hkv, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (N, P, Hkv, D), dtype=np.uint8)
+    pos = [7, 8, 9, 300, 4095, 12]
+    slots = [7, 8, -1, 2 * P + 5, P, N * P]
+    ks, vs = 0.05, 0.02          # |K| / ks and |v| / vs stay below 448 (no saturation)
+    qo, kc2, vc2 = oracle.attention_prologue_fp8(q, k, v, wq, wk, pos, slots, 1e-6, 1e6, 1.0,
+                                                 ks, vs, kc, vc)
+    qb, _, _ = oracle.attention_prologue(q, k, v, wq, wk, pos, slots, 1e-6, 1e6, 1.0,
+                                         np.zeros((N, P, Hkv, D)), np.zeros((N, P, Hkv, D)))
+    assert np.array_equal(qo, qb)
+    kr = oracle.rope_neox(oracle.rms_norm_heads(k, wk, 1e-6), pos, 1e6, 1.0)
+    touched = np.zeros((N, P), bool)
+    for t, sl in enumerate(slots):
+        if not 0 <= sl < N * P:
+            continue
+        page, off = divmod(sl, P)
+        touched[page, off] = True
+        # V: torch's own FP8 cast of the FP32 quotient (an independent rounding)
+        vq = (v[t].float() / torch.tensor(vs, dtype=torch.float32)).to(torch.float8_e4m3fn)
+        assert np.array_equal(vc2[page, off], vq.view(torch.uint8).numpy())
+        # K: within half an E4M3 step of the exact rotated row, plus BF16 rounding
+        dec = oracle.decode_fp8_e4m3(kc2[page, off]) * float(np.float32(ks))
+        err = np.abs(dec - kr[t])
+        assert np.all(err <= (2.0 ** -4 + 2.0 ** -8) * np.abs(kr[t]) * 1.001 + 2.0 ** -10 * ks)
+    assert np.array_equal(kc2[~touched], kc[~touched])
+    assert np.array_equal(vc2[~touched], vc[~touched])
+
+
 def test_planted_mistakes_fail_the_pins():
     # adjacent-pair (GPT-J) rotation and a backwards rotation both miss the
     # worked example; a norm that forgets the weight misses torch's rms_norm
