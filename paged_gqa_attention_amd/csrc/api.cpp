@@ -303,6 +303,8 @@ pa_status_t mq_call(const pa_mq_shape_t* shape, const void* q, const void* k_cac
   a.row_tiles = p.row_tiles;
   a.row_blocks = p.row_blocks;
   a.order_by_work = p.order_by_work;
+  // one row block per KV head: no other workgroup reads a chunk again
+  a.stream_loads = p.row_blocks == 1 && !kv_fp8 ? 1 : 0;
   a.split_pages = p.plan.split_pages;
   a.num_splits = p.plan.num_splits;
   // FP8: K = code * k_scale enters the logits linearly, folded into the score scale

@@ -486,7 +486,12 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // ---- V loads of the first P.V step go out before the softmax ------------
   const int r = lane / LPR;  // token row inside a load instruction
   const int c = lane % LPR;  // 16-byte chunk of the row: dims 8c .. 8c+7
-  // one lane loads the 8 values of dims 8c .. 8c+7 (16 B of BF16, 8 B of FP8)
+  // one lane loads the 8 values of dims 8c .. 8c+7 (16 B of BF16, 8 B of FP8).
+  // Each load instruction reads whole 128-byte lines that nothing reads again:
+  // the loads are marked non-temporal (measured on MI355X: partition kernel
+  // 48.4 -> 45.7 us at batch 16 x 4096, and faster on every other decode
+  // workload). The K tile loads are not: an instruction reads half of each
+  // line and the next one the other half, and marking them cost 2-16%.
   const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 8u * ESZ * c;
   auto load_v = [&](int blk, VChunk (&buf)[PV_U]) __attribute__((always_inline)) {
     const int tl = blk * BR;
@@ -496,7 +501,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     const uint32_t off = (uint32_t)((t0 + tl) % kPage) * row_bytes + v_lane_off;
 #pragma unroll
     for (int u = 0; u < PV_U; ++u)
-      buf[u] = *reinterpret_cast<const VChunk*>(base + off + (uint32_t)(u * RPI) * row_bytes);
+      buf[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const VChunk*>(base + off + (uint32_t)(u * RPI) * row_bytes));
   };
   const int nblk = (n_s + BR - 1) / BR;
   VChunk vbuf[VNB][PV_U];

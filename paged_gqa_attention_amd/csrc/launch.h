@@ -98,6 +98,7 @@ struct MqLaunchArgs {
   int row_tiles;               // 16-row tiles per workgroup: 1, 2, 4 or 8
   int row_blocks;              // workgroups along the rows of one (sequence, KV head)
   int order_by_work;           // 1: dispatch sequences longest first (batch <= 64)
+  int stream_loads;            // 1: K/V staging loads non-temporal (no chunk re-read)
   int split_pages, num_splits;
   float score_scale;           // scale * log2(e) (* k_scale for FP8)
   float v_scale;               // FP8 pools: multiplies the output sums (1 for BF16)
