@@ -231,8 +231,11 @@ _workspaces: dict = {}
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A cached device workspace of at least ``nbytes`` (256-byte aligned)."""
-    key = (device.type, device.index)
+    """A cached device workspace of at least ``nbytes`` (256-byte aligned), one
+    per (device, current stream): calls on one stream run in order and may
+    share it; calls on different streams get different workspaces, and a
+    workspace is only ever allocated, used and replaced on its own stream."""
+    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

@@ -406,3 +406,26 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         assert torch.equal(out.cpu(), eager), rep
         assert torch.equal(run_gpu(w, tensors=t), eager)   # eager work between replays
+
+
+def test_binding_workspace_is_per_stream():
+    # the binding's cached workspace: shared by calls on one stream, separate
+    # for another stream (concurrent calls on two streams must not share it)
+    from paged_gqa_attention_amd import pagedattn as pa
+    dev = torch.device("cuda:0")
+    a = pa._workspace(dev, 4096)
+    assert pa._workspace(dev, 1024) is a
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = pa._workspace(dev, 4096)
+        assert b is not a and b.data_ptr() != a.data_ptr()
+        # a call on the side stream matches the same call on the default stream
+        w = workloads.config(1)
+        t = to_device(w)
+        out_s = pa.pa_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                             t["context_lens"], scale=w.scale)
+    torch.cuda.synchronize()
+    out_d = pa.pa_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+                         scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_d)
