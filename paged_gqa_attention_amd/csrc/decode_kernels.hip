@@ -76,6 +76,12 @@ __host__ __device__ constexpr int wave_tile_words(int split_tokens) {
   return split_tokens * HeadPad<G>::value;
 }
 
+// LDS of a wave's K staging tile (BF16 pools): 16 rows of one head.
+template <int D, bool kFp8>
+__host__ __device__ constexpr int k_stage_bytes() {
+  return kFp8 ? 0 : 16 * D * 2;
+}
+
 // 2 pi as a double plus the remainder, for reducing rotation angles.
 constexpr double k2PiHi = 6.283185307179586;
 constexpr double k2PiLo = 2.4492935982947064e-16;
@@ -254,6 +260,10 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const int s = sg * (kWaves / heads_per_wg) + wave / heads_per_wg;
   const int num_q_heads = num_kv_heads * G;
   float* s_tile = smem + wave * wave_tile_words<G>(split_tokens);  // [token][GP]
+  // BF16 pools: this wave's K staging tile (16 rows of its head, 16-byte
+  // chunks swizzled by row), after the score tiles of all waves
+  char* k_stage = reinterpret_cast<char*>(smem + kWaves * wave_tile_words<G>(split_tokens)) +
+                  wave * k_stage_bytes<D, kFp8>();
 
   // The page ids of the split (lane i: the i-th page it touches), q and the
   // context length load together (one memory round trip, not three). Entries
@@ -426,18 +436,41 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 
   // ---- phase 1: scores = q . K^T on MFMA --------------------------------
   // B operand: lane (lq, lr) holds 8 dims of K[token tl + lr] per k-step (the
-  // dims of its A operand); load j brings bytes 64*j + 16*lq .. +15 of the
-  // row, so one load instruction covers 16 token rows x 64 contiguous bytes.
-  // FP8 codes are widened to BF16 exactly before the MFMA.
-  const uint32_t k_lane_off = (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
+  // dims of its A operand: bytes 64*kk + 16*lq .. +15 of the row for BF16).
+  // BF16 pools: each load instruction reads KRPI whole rows of the head
+  // (lane: row KRPI*j + lane / KCPR, chunk lane % KCPR), non-temporal; the
+  // tile then goes through the wave's LDS staging tile into the operand
+  // layout. Reading 16 rows x 64 bytes per instruction instead (straight
+  // into the operand layout) was slower: measured on MI355X, whole-row loads
+  // made the partition kernel 3-13% faster across the decode workloads, and
+  // only whole-row loads gain from the non-temporal hint.
+  // FP8 pools: load j brings bytes 64*j + 16*lq .. +15 of row lr straight
+  // into the operand layout; codes are widened to BF16 exactly before the MFMA.
+  constexpr bool kStageK = !kFp8;
+  constexpr int KCPR = D * ESZ / 16;  // 16-byte chunks per K row of one head
+  constexpr int KRPI = 64 / KCPR;     // whole rows per load instruction (staged)
+  static_assert(!kStageK || KL * KRPI == 16, "a staged tile is KL load instructions");
+  const uint32_t k_lane_off =
+      kStageK ? (uint32_t)(lane / KCPR) * row_bytes + head_bytes + 16u * (lane % KCPR)
+              : (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
   auto load_k = [&](int tile, u32x4 (&buf)[KL], bool& bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
     take_turn(tl);
     const char* base = page_base(k_cache, tl, bad);
     const uint32_t off = (uint32_t)((t0 + tl) % kPage) * row_bytes + k_lane_off;
 #pragma unroll
-    for (int j = 0; j < KL; ++j)
-      buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
+    for (int j = 0; j < KL; ++j) {
+      if constexpr (kStageK)
+        buf[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(base + off + (uint32_t)(KRPI * j) * row_bytes));
+      else
+        buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
+    }
+  };
+  // LDS byte offsets in the staging tile: chunk c of row r sits at position
+  // c ^ (r % 16) of the row (conflict-free writes and operand reads)
+  auto k_stage_off = [](int r, int c) __attribute__((always_inline)) {
+    return (uint32_t)(r * KCPR + (c ^ (r & 15))) * 16u;
   };
   // running max of the scores this lane holds (heads 4*lq .. 4*lq+3)
   float m_lane[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -447,6 +480,18 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     // the new token's row comes from registers (the pool may still hold the
     // old contents of its slot when this tile was loaded)
     const bool new_row = kStep && tnew >= tl && tnew < tl + 16 && lr == tnew - tl;
+    u32x4 kops[kStageK ? KK : 1];  // staged: the operands read back from LDS
+    if constexpr (kStageK) {
+      // the wave's LDS operations run in order: this tile's writes follow the
+      // previous tile's reads, and the reads below see these writes
+#pragma unroll
+      for (int j = 0; j < KL; ++j)
+        *reinterpret_cast<u32x4*>(k_stage + k_stage_off(KRPI * j + lane / KCPR, lane % KCPR)) =
+            buf[j];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kops[kk] = *reinterpret_cast<const u32x4*>(k_stage + k_stage_off(lr, 4 * kk + lq));
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 kb;
@@ -455,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
         kb = (kk & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
         if (new_row) kb = knew[kk];
       } else {
-        kb = new_row ? knew[kk] : buf[kk];
+        kb = new_row ? knew[kk] : kops[kk];
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
                                                     __builtin_bit_cast(bf16x8, kb), acc, 0, 0, 0);
@@ -718,7 +763,8 @@ int launch_partition_dgt(const LaunchArgs& a) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(a.stream);
   const int hpw = heads_per_workgroup(a.num_kv_heads);
   const dim3 grid(a.batch * (a.num_kv_heads / hpw) * (a.num_splits / (kWaves / hpw)));
-  const size_t lds = sizeof(float) * kWaves * wave_tile_words<G>(a.split_tokens);
+  const size_t lds = sizeof(float) * kWaves * wave_tile_words<G>(a.split_tokens) +
+                     (size_t)kWaves * k_stage_bytes<D, kFp8>();
   void* args[] = {(void*)&a.q,           (void*)&a.k_cache,      (void*)&a.v_cache,
                   (void*)&a.block_table, (void*)&a.context_lens, (void*)&a.ws_acc,
                   (void*)&a.ws_ml,       (void*)&a.batch,        (void*)&a.num_kv_heads,
