@@ -76,10 +76,10 @@ __host__ __device__ constexpr int wave_tile_words(int split_tokens) {
   return split_tokens * HeadPad<G>::value;
 }
 
-// LDS of a wave's K staging tile (BF16 pools): 16 rows of one head.
+// LDS of a wave's K staging tile: 16 rows of one head.
 template <int D, bool kFp8>
 __host__ __device__ constexpr int k_stage_bytes() {
-  return kFp8 ? 0 : 16 * D * 2;
+  return 16 * D * (kFp8 ? 1 : 2);
 }
 
 // 2 pi as a double plus the remainder, for reducing rotation angles.
@@ -260,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   const int s = sg * (kWaves / heads_per_wg) + wave / heads_per_wg;
   const int num_q_heads = num_kv_heads * G;
   float* s_tile = smem + wave * wave_tile_words<G>(split_tokens);  // [token][GP]
-  // BF16 pools: this wave's K staging tile (16 rows of its head, 16-byte
-  // chunks swizzled by row), after the score tiles of all waves
+  // this wave's K staging tile (16 rows of its head, 16-byte chunks swizzled
+  // by row), after the score tiles of all waves
   char* k_stage = reinterpret_cast<char*>(smem + kWaves * wave_tile_words<G>(split_tokens)) +
                   wave * k_stage_bytes<D, kFp8>();
 
@@ -436,17 +436,17 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
 
   // ---- phase 1: scores = q . K^T on MFMA --------------------------------
   // B operand: lane (lq, lr) holds 8 dims of K[token tl + lr] per k-step (the
-  // dims of its A operand: bytes 64*kk + 16*lq .. +15 of the row for BF16).
-  // BF16 pools: each load instruction reads KRPI whole rows of the head
-  // (lane: row KRPI*j + lane / KCPR, chunk lane % KCPR), non-temporal; the
-  // tile then goes through the wave's LDS staging tile into the operand
-  // layout. Reading 16 rows x 64 bytes per instruction instead (straight
-  // into the operand layout) was slower: measured on MI355X, whole-row loads
-  // made the partition kernel 3-13% faster across the decode workloads, and
-  // only whole-row loads gain from the non-temporal hint.
-  // FP8 pools: load j brings bytes 64*j + 16*lq .. +15 of row lr straight
-  // into the operand layout; codes are widened to BF16 exactly before the MFMA.
-  constexpr bool kStageK = !kFp8;
+  // dims of its A operand): chunk 4*kk + lq of the row for BF16, and for FP8
+  // chunk 4*j + lq holds the codes of k-steps 2j and 2j+1.
+  // Each load instruction reads KRPI whole rows of the head (lane: row
+  // KRPI*j + lane / KCPR, chunk lane % KCPR), non-temporal; the tile then goes
+  // through the wave's LDS staging tile into the operand layout. Reading 16
+  // rows x 64 bytes per instruction straight into the operand layout was
+  // slower: measured on MI355X with BF16 pools, whole-row loads made the
+  // partition kernel 4-12% faster across the decode workloads, and only
+  // whole-row loads gain from the non-temporal hint. FP8 codes are widened to
+  // BF16 exactly before the MFMA.
+  constexpr bool kStageK = true;
   constexpr int KCPR = D * ESZ / 16;  // 16-byte chunks per K row of one head
   constexpr int KRPI = 64 / KCPR;     // whole rows per load instruction (staged)
   static_assert(!kStageK || KL * KRPI == 16, "a staged tile is KL load instructions");
@@ -468,9 +468,12 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     }
   };
   // LDS byte offsets in the staging tile: chunk c of row r sits at position
-  // c ^ (r % 16) of the row (conflict-free writes and operand reads)
+  // c ^ (r % 16) of the row, or c ^ ((r / 2) % 8) for 8-chunk rows (FP8 at
+  // D=128, where rows r and r + 8 share banks): writes and operand reads
+  // are then conflict-free.
   auto k_stage_off = [](int r, int c) __attribute__((always_inline)) {
-    return (uint32_t)(r * KCPR + (c ^ (r & 15))) * 16u;
+    const int pos = KCPR >= 16 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+    return (uint32_t)(r * KCPR + pos) * 16u;
   };
   // running max of the scores this lane holds (heads 4*lq .. 4*lq+3)
   float m_lane[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -480,7 +483,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     // the new token's row comes from registers (the pool may still hold the
     // old contents of its slot when this tile was loaded)
     const bool new_row = kStep && tnew >= tl && tnew < tl + 16 && lr == tnew - tl;
-    u32x4 kops[kStageK ? KK : 1];  // staged: the operands read back from LDS
+    constexpr int NOPS = kFp8 ? KL : KK;  // operand chunks per lane and tile
+    u32x4 kops[NOPS];                      // read back from the staging tile
     if constexpr (kStageK) {
       // the wave's LDS operations run in order: this tile's writes follow the
       // previous tile's reads, and the reads below see these writes
@@ -489,18 +493,18 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
         *reinterpret_cast<u32x4*>(k_stage + k_stage_off(KRPI * j + lane / KCPR, lane % KCPR)) =
             buf[j];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
+      for (int kk = 0; kk < NOPS; ++kk)
         kops[kk] = *reinterpret_cast<const u32x4*>(k_stage + k_stage_off(lr, 4 * kk + lq));
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 kb;
       if constexpr (kFp8) {
-        const u32x4 w = buf[kk >> 1];
+        const u32x4 w = kStageK ? kops[kk >> 1] : buf[kk >> 1];
         kb = (kk & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
         if (new_row) kb = knew[kk];
       } else {
-        kb = new_row ? knew[kk] : kops[kk];
+        kb = new_row ? knew[kk] : (kStageK ? kops[kk] : buf[kk]);
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
                                                     __builtin_bit_cast(bf16x8, kb), acc, 0, 0, 0);
