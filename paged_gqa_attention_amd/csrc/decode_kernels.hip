@@ -539,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // Each load instruction reads whole 128-byte lines that nothing reads again:
   // the loads are marked non-temporal (measured on MI355X: partition kernel
   // 48.4 -> 45.7 us at batch 16 x 4096, and faster on every other decode
-  // workload). The K tile loads are not: an instruction reads half of each
-  // line and the next one the other half, and marking them cost 2-16%.
+  // workload), as are the whole-row K loads. Marking K loads that read half
+  // of each line per instruction had cost 2-16%.
   const uint32_t v_lane_off = (uint32_t)r * row_bytes + head_bytes + 8u * ESZ * c;
   auto load_v = [&](int blk, VChunk (&buf)[PV_U]) __attribute__((always_inline)) {
     const int tl = blk * BR;
