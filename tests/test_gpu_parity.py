@@ -429,3 +429,36 @@ def test_binding_workspace_is_per_stream():
                          scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out_s, out_d)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,sp", [(40, 8, 128, 0), (40, 8, 128, 1), (16, 2, 256, 0),
+                                         (16, 2, 256, 2)])
+def test_last_page_of_the_pool(Hq, Hkv, D, sp):
+    # every sequence's last (full) page is one of the pool's last pages, so the
+    # final 16-token tiles of K and V end exactly at the end of the pools
+    from paged_gqa_attention_amd import pagedattn as pa
+    announce(f"last page of the pool {Hq}/{Hkv}/{D} sp{sp}")
+    ctx = [512, 384, 128, 256]
+    w = workloads.build(len(ctx), Hq, Hkv, D, ctx, seed=90 + D + sp, max_pages=4, pool="packed")
+    N = w.k_cache.shape[0]
+    bt = w.block_table.clone()
+    last = [int(bt[b, (c - 1) // 128]) for b, c in enumerate(ctx)]
+    # renumber the pages: sequence i's last page becomes page N - 1 - i, the
+    # others keep their order in the remaining slots
+    target = {p: N - 1 - i for i, p in enumerate(last)}
+    free = [q for q in range(N) if q not in target.values()]
+    perm = [0] * N
+    for p, q in target.items():
+        perm[p] = q
+    for p, q in zip([p for p in range(N) if p not in target], free):
+        perm[p] = q
+    inv = torch.tensor(perm)
+    bt = torch.where(bt >= 0, inv[bt.clamp(min=0)], bt)
+    kc = torch.empty_like(w.k_cache)
+    vc = torch.empty_like(w.v_cache)
+    kc[inv] = w.k_cache
+    vc[inv] = w.v_cache
+    assert sorted(int(bt[b, (c - 1) // 128]) for b, c in enumerate(ctx)) == list(range(N - 4, N))
+    w2 = workloads.Workload(w.name, w.q, kc, vc, bt.to(torch.int32), w.context_lens, w.scale,
+                            dict(w.meta))
+    assert_parity(run_gpu(w2, split_pages=sp), run_oracle(w2), f"last page {D} sp{sp}")
