@@ -462,3 +462,17 @@ def test_last_page_of_the_pool(Hq, Hkv, D, sp):
     w2 = workloads.Workload(w.name, w.q, kc, vc, bt.to(torch.int32), w.context_lens, w.scale,
                             dict(w.meta))
     assert_parity(run_gpu(w2, split_pages=sp), run_oracle(w2), f"last page {D} sp{sp}")
+
+
+@pytest.mark.parametrize("G,Hkv,D,split_pages", [(16, 2, 256, 2), (12, 2, 256, 2), (16, 1, 128, 2)])
+def test_largest_lds_per_workgroup(G, Hkv, D, split_pages):
+    # the largest score tiles the plan allows (16 KiB per wave) plus the K
+    # staging tiles: up to 96 KiB of LDS per partition workgroup at D=256
+    from paged_gqa_attention_amd import pagedattn as pa
+    announce(f"largest LDS G={G} Hkv={Hkv} D={D} sp{split_pages}")
+    ctx = [4096, 1000, 257, 3333]
+    w = workloads.build(len(ctx), G * Hkv, Hkv, D, ctx, seed=500 + G + D, max_pages=32,
+                        pool="permutation")
+    plan = pa.pa_plan(pa.shape_of(w.q, w.k_cache, w.block_table, split_pages))
+    assert plan.split_tokens == 128 * split_pages
+    assert_parity(run_gpu(w, split_pages=split_pages), run_oracle(w), f"largest LDS {G}/{D}")
