@@ -38,13 +38,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 METRIC = "paged GQA decode attention: µs/call and KV-read GB/s (% of HBM peak)"
-KERNEL_SRC = os.path.join(ROOT, "paged_gqa_attention_amd", "csrc", "decode_kernels.hip")
+# the sources the partition kernel is compiled from (its counters go stale when they change)
+KERNEL_SRCS = [os.path.join(ROOT, "paged_gqa_attention_amd", "csrc", n)
+               for n in ("decode_kernels.hip", "device_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_kernel_config3_traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
