@@ -45,10 +45,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_kernel_config3_traffic.
 
 
 def kernel_source_hash() -> str:
+    """Hash of the partition kernel's code: line comments and blank lines are
+    dropped first, so editing a comment does not make the counters stale."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

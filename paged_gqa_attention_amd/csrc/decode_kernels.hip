@@ -18,16 +18,17 @@
 //   head per workgroup). Each wave works alone, with no workgroup barrier:
 //   1. q . K^T on the matrix cores: v_mfma_f32_16x16x32_bf16 with the G query
 //      heads of the group as the 16 rows of A (zero padded) and 16 tokens as
-//      the columns of B. Each lane loads 64 contiguous bytes of one token row
-//      per MFMA k-step, so one load instruction covers 16 rows x 64 B.
-//      Scores are scaled by scale*log2(e) in FP32, tail slots are masked by
-//      select, and the [token][head] score tile goes to the wave's LDS.
+//      the columns of B. Each K load instruction reads whole token rows of
+//      the head (non-temporal); the 16-token tile passes through a per-wave
+//      LDS staging tile into the MFMA operand layout. Scores are scaled by
+//      scale*log2(e) in FP32, tail slots are masked by select, and the
+//      [token][head] score tile goes to the wave's LDS.
 //   2. Per head: max over the split (from running maxima kept in phase 1),
 //      then p = 2^(s - max) and l = sum p in one pass over the wave's LDS tile
 //      (FP32).
 //   3. P.V on the vector ALUs in FP32: each load instruction reads whole token
-//      rows (16 lanes x 16 B for D=128), every lane accumulates G heads x 8
-//      dims, then the rows are summed in a fixed order.
+//      rows (16 lanes x 16 B for D=128, non-temporal), every lane accumulates
+//      G heads x 8 dims, then the rows are summed in a fixed order.
 //   The unnormalised output, the max and the sum of each split go to an FP32
 //   workspace.
 //   reduce_kernel<D>: merges, for every (sequence, query head), the splits that
