@@ -447,26 +447,20 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
   // partition kernel 4-12% faster across the decode workloads, and only
   // whole-row loads gain from the non-temporal hint. FP8 codes are widened to
   // BF16 exactly before the MFMA.
-  constexpr bool kStageK = true;
   constexpr int KCPR = D * ESZ / 16;  // 16-byte chunks per K row of one head
-  constexpr int KRPI = 64 / KCPR;     // whole rows per load instruction (staged)
-  static_assert(!kStageK || KL * KRPI == 16, "a staged tile is KL load instructions");
+  constexpr int KRPI = 64 / KCPR;     // whole rows per load instruction
+  static_assert(KL * KRPI == 16, "a tile is KL load instructions");
   const uint32_t k_lane_off =
-      kStageK ? (uint32_t)(lane / KCPR) * row_bytes + head_bytes + 16u * (lane % KCPR)
-              : (uint32_t)lr * row_bytes + head_bytes + 16u * lq;
+      (uint32_t)(lane / KCPR) * row_bytes + head_bytes + 16u * (lane % KCPR);
   auto load_k = [&](int tile, u32x4 (&buf)[KL], bool& bad) __attribute__((always_inline)) {
     const int tl = tile * 16;
     take_turn(tl);
     const char* base = page_base(k_cache, tl, bad);
     const uint32_t off = (uint32_t)((t0 + tl) % kPage) * row_bytes + k_lane_off;
 #pragma unroll
-    for (int j = 0; j < KL; ++j) {
-      if constexpr (kStageK)
-        buf[j] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(base + off + (uint32_t)(KRPI * j) * row_bytes));
-      else
-        buf[j] = *reinterpret_cast<const u32x4*>(base + off + 64u * j);
-    }
+    for (int j = 0; j < KL; ++j)
+      buf[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(base + off + (uint32_t)(KRPI * j) * row_bytes));
   };
   // LDS byte offsets in the staging tile: chunk c of row r sits at position
   // c ^ (r % 16) of the row, or c ^ ((r / 2) % 8) for 8-chunk rows (FP8 at
@@ -486,26 +480,24 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(
     const bool new_row = kStep && tnew >= tl && tnew < tl + 16 && lr == tnew - tl;
     constexpr int NOPS = kFp8 ? KL : KK;  // operand chunks per lane and tile
     u32x4 kops[NOPS];                      // read back from the staging tile
-    if constexpr (kStageK) {
-      // the wave's LDS operations run in order: this tile's writes follow the
-      // previous tile's reads, and the reads below see these writes
+    // the wave's LDS operations run in order: this tile's writes follow the
+    // previous tile's reads, and the reads below see these writes
 #pragma unroll
-      for (int j = 0; j < KL; ++j)
-        *reinterpret_cast<u32x4*>(k_stage + k_stage_off(KRPI * j + lane / KCPR, lane % KCPR)) =
-            buf[j];
+    for (int j = 0; j < KL; ++j)
+      *reinterpret_cast<u32x4*>(k_stage + k_stage_off(KRPI * j + lane / KCPR, lane % KCPR)) =
+          buf[j];
 #pragma unroll
-      for (int kk = 0; kk < NOPS; ++kk)
-        kops[kk] = *reinterpret_cast<const u32x4*>(k_stage + k_stage_off(lr, 4 * kk + lq));
-    }
+    for (int kk = 0; kk < NOPS; ++kk)
+      kops[kk] = *reinterpret_cast<const u32x4*>(k_stage + k_stage_off(lr, 4 * kk + lq));
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 kb;
       if constexpr (kFp8) {
-        const u32x4 w = kStageK ? kops[kk >> 1] : buf[kk >> 1];
+        const u32x4 w = kops[kk >> 1];
         kb = (kk & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
         if (new_row) kb = knew[kk];
       } else {
-        kb = new_row ? knew[kk] : (kStageK ? kops[kk] : buf[kk]);
+        kb = new_row ? knew[kk] : kops[kk];
       }
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
                                                     __builtin_bit_cast(bf16x8, kb), acc, 0, 0, 0);
